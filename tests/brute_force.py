@@ -1,0 +1,61 @@
+"""Pure-Python brute force for tiny inputs: an implementation of the saliency
+score that shares nothing with the oracle (explicit loops, math.exp,
+math.fsum, per-row softmax written out), used to pin the oracle.
+
+The score is the observation-window attention received by each key: window
+query i of head h sits at position N - w + i, attends causally, and each KV
+head's score is the mean over its G query heads of the window-summed softmax
+(FastKV section 2A saliency; StructKV section 1 attention scores).
+"""
+
+from __future__ import annotations
+
+import math
+
+
+def brute_saliency(q, k, scale):
+    """q: [Hq][w][d], k: [Hkv][N][d] (nested sequences of floats).
+
+    Returns (lse[Hq][w], raw[Hkv][N]) as nested lists of floats.
+    """
+    Hq, w, d = len(q), len(q[0]), len(q[0][0])
+    Hkv, N = len(k), len(k[0])
+    G = Hq // Hkv
+    lse = [[0.0] * w for _ in range(Hq)]
+    raw = [[0.0] * N for _ in range(Hkv)]
+    for h in range(Hq):
+        g = h // G
+        for i in range(w):
+            pos = N - w + i
+            logit = []
+            for j in range(pos + 1):
+                logit.append(scale * math.fsum(q[h][i][t] * k[g][j][t] for t in range(d)))
+            top = max(logit)
+            weights = [math.exp(x - top) for x in logit]
+            total = math.fsum(weights)
+            lse[h][i] = top + math.log(total)
+            for j in range(pos + 1):
+                raw[g][j] += weights[j] / total / G
+    return lse, raw
+
+
+def brute_pool(x, kernel):
+    """Average pool, zero padded, divisor always ``kernel``."""
+    r = (kernel - 1) // 2
+    n = len(x)
+    out = []
+    for j in range(n):
+        acc = []
+        for t in range(j - r, j + r + 1):
+            acc.append(x[t] if 0 <= t < n else 0.0)
+        out.append(math.fsum(acc) / kernel)
+    return out
+
+
+def brute_select(score, n_keys, window, budget):
+    """Largest (budget - window) scores, ties to the lower position, plus the
+    window; ascending."""
+    n_prefix = n_keys - window
+    ranked = sorted(range(n_prefix), key=lambda j: (-score[j], j))
+    kept = sorted(ranked[: budget - window]) + list(range(n_prefix, n_keys))
+    return kept

@@ -1,0 +1,61 @@
+"""Each pin set must catch a plausible mistake planted in a copy of the
+oracle (on the CPU): a dropped term, a wrong sign or index, a transposed
+operand, a wrong divisor, a reversed tie-break."""
+
+import os
+import types
+
+import pytest
+
+import oracle_checks
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "kvsel_oracle.py")
+
+MUTATIONS = {
+    "no_causal_mask": ("future = j > (N - w + i)", "future = j > N"),
+    "causal_off_by_one": ("future = j > (N - w + i)", "future = j >= (N - w + i)"),
+    "no_max_shift": ("z = np.exp(logits - m).sum(axis=1, keepdims=True)\n    return (m + np.log(z))[:, 0]",
+                     "z = np.exp(logits).sum(axis=1, keepdims=True)\n    return np.log(z)[:, 0]"),
+    "lse_sign": ("raw += np.exp(logits - lse[hl][:, None]).sum(axis=0)",
+                 "raw += np.exp(logits + lse[hl][:, None]).sum(axis=0)"),
+    "no_gqa_mean": ("return lse, raw / G", "return lse, raw"),
+    "gqa_interleaved": ("_saliency_group(q[g * G:(g + 1) * G], k[g], scale)",
+                        "_saliency_group(q[g::Hkv], k[g], scale)"),
+    "scale_wrong": ("return 1.0 / math.sqrt(head_dim)", "return 1.0 / head_dim"),
+    "transposed_keys": ("logits = (q_h @ k_g.T) * scale", "logits = (q_h @ k_g[::-1].T) * scale"),
+    "pool_divisor": ("return out / kernel", "return out / max(1, kernel - 1)"),
+    "pool_dropped_tap": ("for t in range(kernel):", "for t in range(kernel - 1):"),
+    "pool_over_window": ("return avg_pool(raw[..., :N - window], kernel)",
+                         "return avg_pool(raw, kernel)[..., :N - window]"),
+    "tie_break_reversed": ("order = np.lexsort((pos, -np.asarray(score, dtype=np.float64)))",
+                           "order = np.lexsort((-pos, -np.asarray(score, dtype=np.float64)))"),
+    "ascending_scores": ("order = np.lexsort((pos, -np.asarray(score, dtype=np.float64)))",
+                         "order = np.lexsort((pos, np.asarray(score, dtype=np.float64)))"),
+    "window_not_kept": ("kept = np.concatenate([np.sort(order[:kk]), np.arange(n_prefix, n_keys)])",
+                        "kept = np.sort(order[:budget])"),
+    "layer_dropped": ("acc = acc + s", "acc = s"),
+    "head_sum": ("return s.mean(axis=-2, keepdims=True)", "return s.sum(axis=-2, keepdims=True)"),
+    "gather_off_by_one": ("out[p] = src[p][idx[p if idx.shape[0] > 1 else 0]]",
+                          "out[p] = src[p][np.minimum(idx[p if idx.shape[0] > 1 else 0] + 1, src.shape[1] - 1)]"),
+    "bf16_widening": ("(b.astype(np.uint32) << 16)", "(b.astype(np.uint32) << 15)"),
+}
+
+
+def _mutant(old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mod = types.ModuleType("kvsel_oracle_mutant")
+    exec(compile(text.replace(old, new), "kvsel_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    mod = _mutant(*MUTATIONS[name])
+    failed = []
+    for check in oracle_checks.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception as e:  # AssertionError, or the mutant blowing up
+            failed.append(check.__name__)
+    assert failed, f"no pin caught mutation {name}"
