@@ -1,0 +1,184 @@
+"""Benchmark: attention-saliency token selection on one MI355X.
+
+One step is the whole path over one batch of seeded synthetic input resident
+in HBM: score every key of every layer (one kvsel_score call that also sums
+the layers), select per KV head (kvsel_topk), gather the kept K and V rows of
+every layer (two kvsel_gather calls). The default workload is the 128K-token
+StructKV-style configuration: 16 layers of 32 query / 8 KV heads x 128,
+N = 131072, w = 32, pool 7, 4096 kept per KV head.
+
+Prints one JSON line (rank 0). ``value`` is keys scored+selected per second
+(layer x sequence x KV head x key units per second of step time).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def _cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, inp, budget_s: float = 15.0) -> dict:
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: the first n layers of every sequence and KV head through
+    score -> accumulate -> select -> gather, n chosen for ~budget_s seconds."""
+    import oracle
+
+    cores = _cores()
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.pipeline(inp["q"][:n], inp["k"][:n], inp["v"][:n], dtype=wl.dtype, window=wl.window,
+                        pool_kernel=wl.pool_kernel, kv_budget=wl.kv_budget, threads=cores)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = 1
+    if t1 < budget_s / 2 and wl.n_layers > 1:
+        n = int(max(1, min(wl.n_layers, round(budget_s / t1))))
+        t = run(n)
+    else:
+        t = t1
+    units = n * wl.batch * wl.n_kv_heads * wl.n_keys
+    return {"value": units / t, "unit": "keys/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {wl.n_layers} layers x {wl.batch} seq x {wl.n_kv_heads} KV heads x {wl.n_keys} keys "
+                      f"(score, layer sum, select, K/V gather) in {t:.1f} s on {cores} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="structkv_128k_16l")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from token_selection_amd import kvsel as K
+    from workloads import get_workload, make_inputs
+
+    wl = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = make_inputs(wl, threads=_cores())
+    print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def up(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
+    B, Hkv, N, w = wl.batch, wl.n_kv_heads, wl.n_keys, wl.window
+    scores = torch.empty((B, Hkv, N - w), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, wl.kv_budget), dtype=torch.int32, device=dev)
+    desc = K.score_desc(q, k, w, wl.pool_kernel)
+    ws = torch.empty(max(1, K.kvsel_score_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+    kc = torch.empty((wl.n_layers, B, Hkv, wl.kv_budget, wl.head_dim), dtype=k.dtype, device=dev)
+    vc = torch.empty_like(kc)
+    stream = torch.cuda.current_stream(dev)
+
+    stages = ("score", "topk", "gather")
+
+    def mk():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(evs=None):
+        # evs: per-stage (start, end) events recorded on the launch stream
+        if evs:
+            evs["score"][0].record(stream)
+        K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
+        if evs:
+            evs["score"][1].record(stream)
+            evs["topk"][0].record(stream)
+        K.kvsel_topk(scores, n_keys=N, window=w, budget=wl.kv_budget, idx=idx)
+        if evs:
+            evs["topk"][1].record(stream)
+            evs["gather"][0].record(stream)
+        K.kvsel_gather(k, idx, kc)
+        K.kvsel_gather(v, idx, vc)
+        if evs:
+            evs["gather"][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K steps back to back, one event pair around all of them
+    # and one around each stage of each step, all on the launch stream
+    per_step = [{n: (mk(), mk()) for n in stages} for _ in range(args.steps)]
+    t_begin, t_end = mk(), mk()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        step(per_step[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    stage_ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in per_step) / args.steps for n in stages}
+
+    cb = wl.compulsory_bytes()
+    units = wl.units
+    value = units / (ms_per_step / 1e3)
+    score_alg_bytes = cb["k_read"] + cb["q_read"] + wl.batch * wl.n_kv_heads * wl.n_prefix * 4
+    achieved = score_alg_bytes / (stage_ms["score"] / 1e3) / 1e9
+    whole_gbs = cb["total"] / (ms_per_step / 1e3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, inp)
+
+    line = {
+        "metric": "keys scored+selected/sec and achieved HBM GB/s (% of peak), 128K ctx",
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; no dataset or weights)",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "q_heads": wl.n_q_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "n_keys": wl.n_keys, "window": wl.window,
+                   "pool": wl.pool_kernel, "kv_budget": wl.kv_budget},
+        "hbm_gbs_whole_path": whole_gbs,
+        "hbm_frac_whole_path": whole_gbs / HBM_PEAK_GBS,
+        "stage_ms": stage_ms,
+        "roofline": {"bound": "hbm", "kernel": "kvsel_score", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,171 @@
+/*
+ * kvsel.h - attention-saliency KV token selection on MI355X (gfx950).
+ *
+ * C ABI of libkvsel.so. Every pointer argument named as device memory must be
+ * memory the caller allocated on the current HIP device (hipMalloc, or a torch
+ * tensor); the library never allocates, frees or keeps a pointer after a call
+ * returns, and it holds no mutable global state. Work is enqueued on the
+ * caller's HIP stream (`stream` is a hipStream_t; NULL means the default
+ * stream) and runs asynchronously; calls on one stream run in order.
+ *
+ * Errors are return codes. Arguments are validated on the host before any
+ * launch; when a call returns anything but KVSEL_OK nothing was enqueued and
+ * no output was written. A launch failure reported by the HIP runtime returns
+ * KVSEL_ERR_HIP. Inputs must be finite (NaN / Inf scores or keys give
+ * unspecified, but memory-safe, results).
+ *
+ * What is computed (the pages: "FastKV: Decoupling of Context Reduction and KV
+ * Cache Compression for Prefill-Decoding Acceleration", section 2A
+ * Token-Selective Propagation and section 2B decoupled KV reduction;
+ * "StructKV: Preserving the Structural Skeleton for Scalable Long-Context
+ * Inference", sections 1 global in-degree centrality and 3 decoupled compute
+ * and storage budgets). With G = Hq / Hkv, query head h reading KV head
+ * floor(h / G), Np = N - w, and window query i sitting at position Np + i:
+ *
+ *   logit[h,i,j] = scale * <q[h,i,:], k[floor(h/G), j, :]>        for j <= Np + i
+ *   p[h,i,j]     = exp(logit[h,i,j] - LSE[h,i])                  (row softmax)
+ *   raw[g,j]     = (1/G) * sum_{h in group g} sum_{i<w} p[h,i,j]  for j < Np
+ *   score[g,j]   = (1/kp) * sum_{t=-r..r} raw[g,j+t]  (raw = 0 outside [0,Np))
+ *   C[g,j]       = sum over layers of score[g,j]                  (StructKV)
+ *   kept         = the (budget - w) prefix positions of largest score, ties to
+ *                  the lower position, plus the window Np .. N-1, ascending.
+ */
+#ifndef KVSEL_H_
+#define KVSEL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvsel_status_t;
+
+#define KVSEL_OK 0              /* success */
+#define KVSEL_ERR_INVALID_ARG 1 /* a null pointer, bad size, bad stride or alignment */
+#define KVSEL_ERR_UNSUPPORTED 2 /* valid but not implemented: head_dim, dtype, pool type */
+#define KVSEL_ERR_WORKSPACE 3   /* workspace missing or smaller than the queried size */
+#define KVSEL_ERR_HIP 4         /* the HIP runtime reported a launch error */
+
+#define KVSEL_DTYPE_F32 0  /* IEEE binary32 */
+#define KVSEL_DTYPE_BF16 1 /* bfloat16 (upper half of a binary32) */
+
+#define KVSEL_POOL_AVG 0 /* stride-1 average pool, zero padded, divisor = kernel */
+
+#define KVSEL_ACC_ADD 0       /* dst[b,h,:] += src[b,h,:] */
+#define KVSEL_ACC_HEAD_MEAN 1 /* dst[b,0,:]  = mean over h of src[b,h,:] */
+
+/*
+ * Shape of one scoring call. Q holds the w window queries of every layer,
+ * sequence and query head, post-RoPE: element (l, b, h, i, e) lives at
+ * q_win + l*q_strides[0] + b*q_strides[1] + h*q_strides[2] + i*q_strides[3] + e
+ * (strides in elements; the head-dim stride is 1), so q_win may be a strided
+ * view of the caller's full query tensor. K is addressed the same way with
+ * k_strides over (layer, b, kv_head, position).
+ */
+typedef struct kvsel_score_desc {
+    int32_t n_layers;    /* L >= 1: layers scored and summed in this call */
+    int32_t batch;       /* B >= 1 */
+    int32_t n_q_heads;   /* Hq >= 1, a multiple of n_kv_heads */
+    int32_t n_kv_heads;  /* Hkv >= 1; L * B * Hkv <= 65535 */
+    int32_t head_dim;    /* d: 64 or 128 (others: KVSEL_ERR_UNSUPPORTED) */
+    int32_t window;      /* w: 1 <= w <= n_keys */
+    int64_t n_keys;      /* N: cached keys per sequence, N < 2^31 */
+    int32_t pool_kernel; /* odd, >= 1 (1 = no pool), <= 255 */
+    int32_t pool_type;   /* KVSEL_POOL_AVG */
+    int32_t dtype;       /* KVSEL_DTYPE_F32 or KVSEL_DTYPE_BF16, for Q and K */
+    float softmax_scale; /* > 0, or <= 0 for 1/sqrt(head_dim) */
+    int64_t q_strides[4];
+    int64_t k_strides[4];
+} kvsel_score_desc_t;
+
+/* Device workspace, in bytes, that kvsel_score needs for `desc` (0 on an
+ * invalid descriptor). */
+size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc);
+
+/*
+ * Saliency scores of every prefix key (FastKV section 2A; StructKV section 1).
+ *
+ * q_win   device, see kvsel_score_desc_t; 16-byte aligned rows.
+ * k       device, see kvsel_score_desc_t; 16-byte aligned rows.
+ * scores  device float[B][Hkv][N - w], contiguous. accumulate == 0: written
+ *         with the sum over the L layers of the pooled score; accumulate != 0:
+ *         that sum is added to what scores holds (StructKV accumulation across
+ *         calls, layer by layer or in groups of layers).
+ * lse_out device float[L][B][Hq][w] or NULL: the natural-log LSE of every
+ *         window row.
+ * workspace  device, >= kvsel_score_workspace_bytes(desc) bytes, 256-byte
+ *         aligned; its content is scratch between calls.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
+                           int32_t accumulate, float* lse_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Accumulate score vectors (StructKV section 1: a token's scores added up over
+ * layers; FastKV section 2A: one token set per sequence for propagation).
+ *
+ * src  device float[batch][n_heads][n]; dst device float.
+ * KVSEL_ACC_ADD:       dst[batch][n_heads][n] += src.
+ * KVSEL_ACC_HEAD_MEAN: dst[batch][1][n] = (1/n_heads) * sum over heads of src
+ *                      (the token-set score ranked for propagation).
+ * src and dst must not overlap. Errors: INVALID_ARG, HIP.
+ */
+kvsel_status_t kvsel_accumulate(int32_t batch, int32_t n_heads, int64_t n, const float* src, float* dst,
+                                int32_t mode, void* stream);
+
+/* Device workspace, in bytes, that kvsel_topk needs (0 on invalid sizes). */
+size_t kvsel_topk_workspace_bytes(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget);
+
+/*
+ * Keep `budget` positions per selection row (FastKV section 2A: the most
+ * salient tokens plus a window of the newest; section 2B and StructKV section
+ * 3: the TSP / compute budget and the KV / storage budget are separate calls).
+ *
+ * scores  device float[batch][rows][n_keys - window], contiguous, >= 0.
+ * idx     device int32[batch][rows][budget], contiguous: per row the
+ *         (budget - window) prefix positions with the largest score (ties go
+ *         to the lower position), then window positions n_keys - window ..
+ *         n_keys - 1; strictly ascending, window last.
+ * The TSP token set calls this with rows = 1 on the head-mean score; the KV
+ * set with rows = n_kv_heads.
+ * Preconditions: 1 <= window <= budget <= n_keys < 2^31; batch * rows <= 2^31-1.
+ * Errors: INVALID_ARG, WORKSPACE, HIP.
+ */
+kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
+                          const float* scores, int32_t* idx, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * Compact the cache (FastKV section 2A: only the kept tokens are passed on;
+ * section 2B / StructKV section 3: the kept KV entries are stored).
+ *
+ * Copies rows bit for bit: dst[l][b][h][t][:] = src row (l, b, h,
+ * idx[b][idx_heads == 1 ? 0 : h][t]) for every layer l < n_layers; a row is
+ * `row_bytes` bytes. The source row (l, b, h, j) starts at
+ * src + l*s[0] + b*s[1] + h*s[2] + j*s[3] bytes, s = src_strides_bytes.
+ * dst is device memory, contiguous [n_layers][batch][n_heads][budget][row_bytes].
+ * idx is device int32[batch][idx_heads][budget] with idx_heads 1 (one token set
+ * shared by every head, e.g. hidden states) or n_heads (per KV head). An index
+ * outside [0, n_src_rows) yields an all-zero row.
+ * Rows whose size, base and strides are multiples of 16 bytes are copied with
+ * 16-byte accesses, otherwise byte by byte. src and dst must not overlap.
+ * Errors: INVALID_ARG, HIP.
+ */
+kvsel_status_t kvsel_gather(int32_t n_layers, int32_t batch, int32_t n_heads, int32_t idx_heads, int32_t budget,
+                            int64_t n_src_rows, int64_t row_bytes, const void* src,
+                            const int64_t src_strides_bytes[4], const int32_t* idx, void* dst, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* kvsel_status_string(kvsel_status_t status);
+
+/* Library version string. */
+const char* kvsel_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H_ */

@@ -1,0 +1,163 @@
+"""The C-ABI library: it loads, exports every function include/kvsel.h
+declares, its struct layout matches the binding, and every argument error is
+reported before any launch (these calls never reach the GPU). CPU only."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvsel.h")
+
+kvsel = pytest.importorskip("token_selection_amd.kvsel")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kvsel.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvsel_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(kvsel.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", kvsel.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kvsel_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_struct_layout_matches_header():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "kvsel.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(kvsel_score_desc_t), offsetof(kvsel_score_desc_t, n_keys),
+         offsetof(kvsel_score_desc_t, pool_kernel), offsetof(kvsel_score_desc_t, softmax_scale),
+         offsetof(kvsel_score_desc_t, q_strides), offsetof(kvsel_score_desc_t, k_strides));
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    D = kvsel.ScoreDesc
+    assert got == [ctypes.sizeof(D), D.n_keys.offset, D.pool_kernel.offset, D.softmax_scale.offset,
+                   D.q_strides.offset, D.k_strides.offset]
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert kvsel.status_string(code).startswith("KVSEL")
+    assert "unknown" in kvsel.status_string(99)
+    assert "gfx950" in kvsel.version()
+
+
+def good_desc(**kw):
+    d = kvsel.ScoreDesc()
+    d.n_layers, d.batch, d.n_q_heads, d.n_kv_heads = 1, 1, 8, 2
+    d.head_dim, d.window, d.n_keys = 128, 8, 1024
+    d.pool_kernel, d.pool_type, d.dtype, d.softmax_scale = 7, 0, kvsel.KVSEL_DTYPE_BF16, 0.0
+    q = [4 * 8 * 128, 4 * 8 * 128, 8 * 128, 128]
+    k = [2 * 1024 * 128, 2 * 1024 * 128, 1024 * 128, 128]
+    for i in range(4):
+        d.q_strides[i] = q[i]
+        d.k_strides[i] = k[i]
+    for key, v in kw.items():
+        if key in ("q_strides", "k_strides"):
+            for i in range(4):
+                getattr(d, key)[i] = v[i]
+        else:
+            setattr(d, key, v)
+    return d
+
+
+FAKE = 1 << 32  # a 256-byte aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_layers", 0, 1), ("batch", 0, 1), ("n_q_heads", 7, 1), ("n_kv_heads", 0, 1),
+    ("window", 0, 1), ("n_keys", 4, 1), ("n_keys", 1 << 31, 1),
+    ("pool_kernel", 4, 1), ("pool_kernel", 0, 1), ("pool_kernel", 257, 1),
+    ("softmax_scale", float("inf"), 1), ("softmax_scale", float("nan"), 1),
+    ("head_dim", 96, 2), ("dtype", 7, 2), ("pool_type", 1, 2),
+    ("k_strides", [0, 0, 1024 * 128, 127], 1), ("q_strides", [0, 0, -128, 128], 1),
+])
+def test_score_rejects_bad_descriptor(lib, field, value, status):
+    d = good_desc(**{field: value})
+    assert lib.kvsel_score_workspace_bytes(ctypes.byref(d)) == 0
+    st = lib.kvsel_score(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, FAKE, 1 << 40, None)
+    assert st == status
+
+
+def test_score_rejects_pointers_and_workspace(lib):
+    d = good_desc()
+    need = lib.kvsel_score_workspace_bytes(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    assert lib.kvsel_score(None, FAKE, FAKE, FAKE, 0, None, FAKE, need, None) == 1
+    assert lib.kvsel_score(ctypes.byref(d), None, FAKE, FAKE, 0, None, FAKE, need, None) == 1
+    assert lib.kvsel_score(ctypes.byref(d), FAKE + 8, FAKE, FAKE, 0, None, FAKE, need, None) == 1
+    assert lib.kvsel_score(ctypes.byref(d), FAKE, FAKE, None, 0, None, FAKE, need, None) == 1
+    assert lib.kvsel_score(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, None, need, None) == 3
+    assert lib.kvsel_score(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, FAKE, need - 1, None) == 3
+    assert lib.kvsel_score(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, FAKE + 16, need, None) == 3
+
+
+def test_workspace_grows_with_problem(lib):
+    small = lib.kvsel_score_workspace_bytes(ctypes.byref(good_desc()))
+    big = lib.kvsel_score_workspace_bytes(ctypes.byref(good_desc(n_layers=4, n_keys=4096,
+                                                                 k_strides=[2 * 4096 * 128, 2 * 4096 * 128, 4096 * 128, 128])))
+    assert big > small
+
+
+@pytest.mark.parametrize("args", [
+    (0, 1, 100, 4, 10), (1, 0, 100, 4, 10), (1, 1, 100, 0, 10), (1, 1, 100, 4, 3),
+    (1, 1, 100, 4, 101), (1, 1, 1 << 31, 4, 10), (1 << 16, 1 << 16, 100, 4, 10),
+])
+def test_topk_rejects(lib, args):
+    B, rows, N, w, budget = args
+    assert lib.kvsel_topk(B, rows, N, w, budget, FAKE, FAKE, None, 0, None) == 1
+
+
+def test_topk_rejects_null(lib):
+    assert lib.kvsel_topk(1, 1, 100, 4, 10, None, FAKE, None, 0, None) == 1
+    assert lib.kvsel_topk(1, 1, 100, 4, 10, FAKE, None, None, 0, None) == 1
+
+
+def test_gather_rejects(lib):
+    s = (ctypes.c_int64 * 4)(0, 0, 256, 256)
+    ok = (1, 1, 2, 2, 8, 100, 256, FAKE, s, FAKE, FAKE, None)
+    bad = [
+        (0,) + ok[1:], ok[:1] + (0,) + ok[2:], ok[:3] + (3,) + ok[4:], ok[:4] + (0,) + ok[5:],
+        ok[:5] + (0,) + ok[6:], ok[:6] + (0,) + ok[7:], ok[:7] + (None,) + ok[8:],
+        ok[:8] + (None,) + ok[9:], ok[:9] + (None,) + ok[10:], ok[:10] + (None,) + ok[11:],
+    ]
+    for args in bad:
+        assert lib.kvsel_gather(*args) == 1
+    neg = (ctypes.c_int64 * 4)(0, 0, -256, 256)
+    assert lib.kvsel_gather(*(ok[:8] + (neg,) + ok[9:])) == 1
+
+
+def test_accumulate_rejects(lib):
+    assert lib.kvsel_accumulate(1, 1, 10, FAKE, FAKE, 2, None) == 1
+    assert lib.kvsel_accumulate(0, 1, 10, FAKE, FAKE, 0, None) == 1
+    assert lib.kvsel_accumulate(1, 1, -1, FAKE, FAKE, 0, None) == 1
+    assert lib.kvsel_accumulate(1, 1, 10, None, FAKE, 0, None) == 1
+
+
+def test_rate_helper():
+    assert kvsel.budget_from_rate(0.1, 32768, 32) == 3277

@@ -1,0 +1,177 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs at sizes
+the oracle finishes in seconds: the tiny fp32 workload in full, ragged and
+degenerate shapes that span several tiles, accumulation, the token-set path,
+exact ties, large logits, determinism and output coverage."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (assert_gather, assert_scores_close, assert_selection, check_all, device, oracle_for,
+                      run_gpu, say, to_dev)
+from token_selection_amd import kvsel as K
+from workloads import get_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TINY = get_workload("tiny_f32_2k")
+
+
+def test_tiny_workload_full():
+    say("case tiny_f32_2k full")
+    inp = make_inputs(TINY)
+    gpu = run_gpu(TINY, inp)
+    ref = oracle_for(TINY, inp)
+    check_all(TINY, inp, gpu, ref)
+    # behaviour (not parity): the 16 planted hubs are kept in both heads
+    hubs = inp["hub_pos"]
+    for g in range(TINY.n_kv_heads):
+        assert set(hubs) <= set(gpu["idx"][0, g].tolist())
+
+
+# (dtype, L, B, Hq, Hkv, d, N, w, pool, budget)
+RAGGED = [
+    ("bf16", 1, 1, 4, 1, 128, 3001, 5, 7, 300),     # ragged last chunk, G=4, w=5 -> 20 rows
+    ("bf16", 2, 2, 6, 2, 64, 2500, 7, 3, 999),      # G=3, 21 rows, 2 layers
+    ("bf16", 1, 1, 28, 4, 128, 4100, 16, 7, 512),   # G=7 -> 112 rows (7 row blocks)
+    ("bf16", 1, 1, 14, 1, 128, 1500, 20, 7, 100),   # 280 rows -> 3 row groups
+    ("bf16", 1, 1, 8, 8, 128, 1111, 1, 1, 1),       # w=1, budget=w, G=1
+    ("bf16", 1, 1, 8, 2, 128, 777, 64, 5, 777),     # budget = N
+    ("bf16", 1, 2, 4, 2, 128, 40, 40, 7, 40),       # w = N: empty prefix
+    ("bf16", 1, 1, 4, 2, 128, 41, 40, 7, 41),       # one prefix key
+    ("f32", 1, 1, 8, 2, 64, 2049, 32, 7, 256),      # fp32, ragged
+    ("f32", 3, 1, 4, 2, 128, 1300, 9, 3, 60),       # fp32 d=128, 3 layers
+    ("f32", 1, 1, 12, 4, 64, 5000, 33, 1, 4000),    # fp32, pool 1, large budget
+    ("bf16", 1, 1, 64, 8, 128, 2048, 128, 7, 1024), # 1024 rows -> 8 groups
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "-".join(map(str, c)))
+def test_ragged_shapes(case):
+    dt, L, B, Hq, Hkv, d, N, w, pool, budget = case
+    say("case ragged", case)
+    wl = TINY.with_(name="ragged", wid=100 + RAGGED.index(case), dtype=dt, n_layers=L, batch=B, n_q_heads=Hq,
+                    n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool, kv_budget=budget,
+                    n_hubs=min(8, max(0, N - w - 1)))
+    inp = make_inputs(wl)
+    gpu = run_gpu(wl, inp)
+    ref = oracle_for(wl, inp)
+    check_all(wl, inp, gpu, ref)
+
+
+def test_rope_sink_tsp_small():
+    """The token-set (TSP) path on a reduced 32K-style layer: RoPE, a sink,
+    hubs, head mean, one token set per sequence, hidden-row gather."""
+    wl = get_workload("llama8b_32k_tsp").with_(n_keys=6000, n_hubs=60, hidden_dim=136, batch=2,
+                                               kv_budget=300, tsp_budget=700)
+    say("case tsp small")
+    inp = make_inputs(wl)
+    gpu = run_gpu(wl, inp)
+    ref = oracle_for(wl, inp)
+    check_all(wl, inp, gpu, ref)
+    assert 0 in gpu["tsp_idx"][0, 0]  # the sink survives
+
+
+def test_accumulate_flag_adds_layers():
+    """scores(accumulate) = previous content + this call's layer sum; two
+    calls of 2 layers equal one call of 4 layers (StructKV accumulation)."""
+    wl = TINY.with_(name="acc", wid=140, dtype="bf16", head_dim=128, n_layers=4, n_keys=3000, window=16,
+                    kv_budget=400, hub_mode="norm", hub_scale=3.0, hub_layers=1, n_hubs=20)
+    say("case accumulate")
+    inp = make_inputs(wl)
+    ref = oracle_for(wl, inp)
+    q = to_dev(inp["q"], "bf16")
+    k = to_dev(inp["k"], "bf16")
+    s1 = K.kvsel_score(q[:2], k[:2], window=wl.window, pool_kernel=7)
+    K.kvsel_score(q[2:], k[2:], s1, window=wl.window, pool_kernel=7, accumulate=True)
+    s4 = K.kvsel_score(q, k, window=wl.window, pool_kernel=7)
+    torch.cuda.synchronize()
+    assert_scores_close(s1.cpu().numpy(), ref["scores"])
+    assert_scores_close(s4.cpu().numpy(), ref["scores"])
+    # one layer at a time through kvsel_accumulate(ADD)
+    acc = torch.zeros_like(s4)
+    for l in range(4):
+        sl = K.kvsel_score(q[l], k[l], window=wl.window, pool_kernel=7)
+        K.kvsel_accumulate(sl, acc, K.KVSEL_ACC_ADD)
+    torch.cuda.synchronize()
+    assert_scores_close(acc.cpu().numpy(), ref["scores"])
+
+
+def test_exact_ties_follow_tie_break():
+    """q = 0 makes every prefix score bit-identical on the GPU too; the
+    tie-break alone decides: pool 1 keeps [0, kk), pool 7 keeps [3, kk + 3)."""
+    for pool, first in ((1, 0), (7, 3)):
+        wl = TINY.with_(name="ties", wid=150, dtype="bf16", head_dim=128, query_model="zero", n_keys=5000,
+                        window=24, pool_kernel=pool, kv_budget=1000, n_hubs=0, hub_mode=None)
+        say("case ties pool", pool)
+        inp = make_inputs(wl)
+        gpu = run_gpu(wl, inp, with_gather=False)
+        kk = wl.kv_budget - wl.window
+        exp = list(range(first, first + kk)) + list(range(wl.n_prefix, wl.n_keys))
+        for g in range(wl.n_kv_heads):
+            assert gpu["idx"][0, g].tolist() == exp
+            interior = gpu["scores"][0, g, 3:-3]
+            assert np.all(interior == interior[0])
+        ref = oracle_for(wl, inp)
+        assert_scores_close(gpu["scores"], ref["scores"])
+
+
+def test_large_logits_are_stable():
+    """Keys x 100 push logits to about +-1000: the two-pass softmax must
+    subtract row maxima (fp32 exp overflows past 88)."""
+    wl = TINY.with_(name="big", wid=160, dtype="bf16", head_dim=128, k_mult=100.0, n_keys=3000, window=16,
+                    kv_budget=200, n_hubs=0, hub_mode=None)
+    say("case large logits")
+    inp = make_inputs(wl)
+    gpu = run_gpu(wl, inp)
+    ref = oracle_for(wl, inp)
+    assert np.abs(ref["lse"]).max() > 500
+    check_all(wl, inp, gpu, ref)
+
+
+def test_deterministic_and_fully_written():
+    """Two runs give bit-identical scores and indices; outputs pre-filled with
+    NaN / -1 are fully overwritten and guard bands around them stay intact."""
+    wl = get_workload("llama8b_32k_tsp").with_(n_keys=9000, n_hubs=90, tsp_budget=None, hidden_dim=None,
+                                               kv_budget=700)
+    say("case determinism")
+    inp = make_inputs(wl, with_v=False)
+    q = to_dev(inp["q"], "bf16")
+    k = to_dev(inp["k"], "bf16")
+    B, H, Np = 1, wl.n_kv_heads, wl.n_prefix
+    guard = 4096
+    runs = []
+    for rep in range(2):
+        sbuf = torch.full((B * H * Np + 2 * guard,), float("nan"), device=device())
+        ibuf = torch.full((B * H * wl.kv_budget + 2 * guard,), -7, dtype=torch.int32, device=device())
+        scores = sbuf[guard:guard + B * H * Np].view(B, H, Np)
+        idx = ibuf[guard:guard + B * H * wl.kv_budget].view(B, H, wl.kv_budget)
+        K.kvsel_score(q, k, scores, window=wl.window, pool_kernel=7)
+        K.kvsel_topk(scores, n_keys=wl.n_keys, window=wl.window, budget=wl.kv_budget, idx=idx)
+        torch.cuda.synchronize()
+        sb, ib = sbuf.cpu().numpy(), ibuf.cpu().numpy()
+        assert np.isnan(sb[:guard]).all() and np.isnan(sb[-guard:]).all()
+        assert (ib[:guard] == -7).all() and (ib[-guard:] == -7).all()
+        assert np.isfinite(sb[guard:-guard]).all()
+        assert (ib[guard:-guard] >= 0).all()
+        runs.append((sb[guard:-guard].copy(), ib[guard:-guard].copy()))
+    assert runs[0][0].tobytes() == runs[1][0].tobytes()
+    assert np.array_equal(runs[0][1], runs[1][1])
+
+
+def test_strided_query_view():
+    """q_win may be a strided view of a larger query tensor (only the last w
+    positions of every head)."""
+    wl = TINY.with_(name="strided", wid=170, dtype="bf16", head_dim=128, n_keys=2500, window=12, kv_budget=100)
+    say("case strided q")
+    inp = make_inputs(wl, with_v=False)
+    L, B, Hq, w, d = inp["q"].shape
+    big = np.zeros((L, B, Hq, 50, d), dtype=np.uint16)
+    big[:, :, :, 50 - w:] = inp["q"]
+    qbig = to_dev(big, "bf16")
+    k = to_dev(inp["k"], "bf16")
+    s = K.kvsel_score(qbig[:, :, :, 50 - w:], k, window=w, pool_kernel=7)
+    torch.cuda.synchronize()
+    ref = oracle_for(wl, inp)
+    assert_scores_close(s.cpu().numpy(), ref["scores"])

@@ -1,0 +1,169 @@
+// C ABI of libkvsel: argument validation, geometry, kernel dispatch.
+//
+// Every entry point validates its arguments on the host before enqueuing any
+// work, so an error return means nothing was launched and nothing written.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kvsel.h"
+#include "kvsel_internal.h"
+
+using kvsel::ScoreGeom;
+using kvsel::ScoreWs;
+
+namespace {
+
+constexpr int64_t kMaxKeys = (int64_t)1 << 31;  // positions are int32 on the device
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+kvsel_status_t validate_desc(const kvsel_score_desc_t* d) {
+    if (!d) return KVSEL_ERR_INVALID_ARG;
+    if (d->n_layers < 1 || d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return KVSEL_ERR_INVALID_ARG;
+    if (d->n_q_heads % d->n_kv_heads != 0) return KVSEL_ERR_INVALID_ARG;
+    if (d->window < 1 || d->n_keys < d->window || d->n_keys >= kMaxKeys) return KVSEL_ERR_INVALID_ARG;
+    if (d->pool_kernel < 1 || d->pool_kernel % 2 == 0 || d->pool_kernel > 255) return KVSEL_ERR_INVALID_ARG;
+    if ((int64_t)d->n_layers * d->batch * d->n_kv_heads > 65535) return KVSEL_ERR_INVALID_ARG;
+    if ((int64_t)(d->n_q_heads / d->n_kv_heads) * d->window > (1 << 20)) return KVSEL_ERR_INVALID_ARG;
+    if (!isfinite(d->softmax_scale)) return KVSEL_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i)
+        if (d->q_strides[i] < 0 || d->k_strides[i] < 0) return KVSEL_ERR_INVALID_ARG;
+    if (d->dtype != KVSEL_DTYPE_F32 && d->dtype != KVSEL_DTYPE_BF16) return KVSEL_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
+    if (d->pool_type != KVSEL_POOL_AVG) return KVSEL_ERR_UNSUPPORTED;
+    const int64_t e = d->dtype == KVSEL_DTYPE_F32 ? 4 : 2;
+    for (int i = 0; i < 4; ++i)
+        if ((d->q_strides[i] * e) % 16 != 0 || (d->k_strides[i] * e) % 16 != 0) return KVSEL_ERR_INVALID_ARG;
+    return KVSEL_OK;
+}
+
+void make_geom(const kvsel_score_desc_t* d, ScoreGeom& g, int& RB) {
+    g.L = d->n_layers;
+    g.B = d->batch;
+    g.Hq = d->n_q_heads;
+    g.Hkv = d->n_kv_heads;
+    g.G = d->n_q_heads / d->n_kv_heads;
+    g.w = d->window;
+    g.R = g.G * g.w;
+    RB = kvsel::score_row_blocks(d->dtype, d->head_dim, g.R);
+    const int nb = (g.R + 15) / 16;
+    g.n_groups = (nb + RB - 1) / RB;
+    g.Rpad = g.n_groups * RB * 16;
+    g.S = g.L * g.B * g.Hkv;
+    g.N = d->n_keys;
+    g.Np = d->n_keys - d->window;
+    g.chunk = kvsel::kScoreChunk;
+    g.n_chunks1 = (int32_t)((g.N + g.chunk - 1) / g.chunk);
+    g.n_chunks2 = (int32_t)((g.Np + g.chunk - 1) / g.chunk);
+    const double scale = d->softmax_scale > 0.f ? (double)d->softmax_scale : 1.0 / sqrt((double)d->head_dim);
+    g.c = (float)(scale * 1.4426950408889634074);  // log2(e)
+    g.invG = (float)(1.0 / (double)g.G);
+    for (int i = 0; i < 4; ++i) {
+        g.qs[i] = d->q_strides[i];
+        g.ks[i] = d->k_strides[i];
+    }
+    g.q = nullptr;
+    g.k = nullptr;
+    g.part = nullptr;
+    g.lse2 = nullptr;
+    g.raw = nullptr;
+    g.lse_out = nullptr;
+}
+
+ScoreWs ws_layout(const ScoreGeom& g) { return kvsel::score_workspace_layout(g.S, g.n_chunks1, g.Rpad, g.Np); }
+
+kvsel_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvsel_status_string(kvsel_status_t status) {
+    switch (status) {
+        case KVSEL_OK: return "KVSEL_OK";
+        case KVSEL_ERR_INVALID_ARG: return "KVSEL_ERR_INVALID_ARG: invalid argument";
+        case KVSEL_ERR_UNSUPPORTED: return "KVSEL_ERR_UNSUPPORTED: unsupported head_dim, dtype or pool type";
+        case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE: workspace missing or too small";
+        case KVSEL_ERR_HIP: return "KVSEL_ERR_HIP: HIP runtime error";
+        default: return "KVSEL: unknown status";
+    }
+}
+
+const char* kvsel_version(void) { return "kvsel 0.1.0 (gfx950)"; }
+
+size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc) {
+    if (validate_desc(desc) != KVSEL_OK) return 0;
+    ScoreGeom g;
+    int RB;
+    make_geom(desc, g, RB);
+    return ws_layout(g).total;
+}
+
+kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
+                           int32_t accumulate, float* lse_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    const kvsel_status_t st = validate_desc(desc);
+    if (st != KVSEL_OK) return st;
+    if (!q_win || !k || !aligned16(q_win) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
+    if (desc->n_keys > desc->window && !scores) return KVSEL_ERR_INVALID_ARG;
+    ScoreGeom g;
+    int RB;
+    make_geom(desc, g, RB);
+    const ScoreWs lay = ws_layout(g);
+    if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    g.q = q_win;
+    g.k = k;
+    g.part = reinterpret_cast<float2*>(ws + lay.part_off);
+    g.lse2 = reinterpret_cast<float*>(ws + lay.lse2_off);
+    g.raw = reinterpret_cast<float*>(ws + lay.raw_off);
+    g.lse_out = lse_out;
+    return from_hip(kvsel::launch_score(g, desc->dtype, desc->head_dim, RB, scores, accumulate ? 1 : 0,
+                                        desc->pool_kernel, static_cast<hipStream_t>(stream)));
+}
+
+kvsel_status_t kvsel_accumulate(int32_t batch, int32_t n_heads, int64_t n, const float* src, float* dst,
+                                int32_t mode, void* stream) {
+    if (batch < 1 || n_heads < 1 || n < 0 || !src || !dst) return KVSEL_ERR_INVALID_ARG;
+    if (mode != KVSEL_ACC_ADD && mode != KVSEL_ACC_HEAD_MEAN) return KVSEL_ERR_INVALID_ARG;
+    return from_hip(kvsel::launch_accumulate(batch, n_heads, n, src, dst, mode, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvsel_topk_workspace_bytes(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget) {
+    (void)batch;
+    (void)rows;
+    (void)n_keys;
+    (void)window;
+    (void)budget;
+    return 0;  // the single-work-group-per-row select keeps its state in LDS
+}
+
+kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
+                          const float* scores, int32_t* idx, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (batch < 1 || rows < 1 || (int64_t)batch * rows > INT32_MAX) return KVSEL_ERR_INVALID_ARG;
+    if (window < 1 || budget < window || n_keys < budget || n_keys >= kMaxKeys) return KVSEL_ERR_INVALID_ARG;
+    if (!idx || (n_keys > window && !scores)) return KVSEL_ERR_INVALID_ARG;
+    return from_hip(kvsel::launch_topk(batch * rows, n_keys, window, budget, scores, idx,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+kvsel_status_t kvsel_gather(int32_t n_layers, int32_t batch, int32_t n_heads, int32_t idx_heads, int32_t budget,
+                            int64_t n_src_rows, int64_t row_bytes, const void* src,
+                            const int64_t src_strides_bytes[4], const int32_t* idx, void* dst, void* stream) {
+    if (n_layers < 1 || batch < 1 || n_heads < 1 || budget < 1 || n_src_rows < 1 || row_bytes < 1)
+        return KVSEL_ERR_INVALID_ARG;
+    if (idx_heads != 1 && idx_heads != n_heads) return KVSEL_ERR_INVALID_ARG;
+    if (!src || !dst || !idx || !src_strides_bytes) return KVSEL_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i)
+        if (src_strides_bytes[i] < 0) return KVSEL_ERR_INVALID_ARG;
+    return from_hip(kvsel::launch_gather(n_layers, batch, n_heads, idx_heads, budget, n_src_rows, row_bytes, src,
+                                         src_strides_bytes, idx, dst, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
