@@ -119,8 +119,8 @@ def assert_selection(idx_gpu: np.ndarray, scores_gpu: np.ndarray, scores_ref: np
     """idx_gpu [..., budget]; scores [..., N - w]."""
     lead = idx_gpu.shape[:-1]
     ig = idx_gpu.reshape(-1, budget).astype(np.int64)
-    sg = scores_gpu.reshape(-1, n_keys - window).astype(np.float64)
-    sr = scores_ref.reshape(-1, n_keys - window)
+    sg = scores_gpu.reshape(ig.shape[0], n_keys - window).astype(np.float64)
+    sr = scores_ref.reshape(ig.shape[0], n_keys - window)
     kk = budget - window
     for r in range(ig.shape[0]):
         row = ig[r]

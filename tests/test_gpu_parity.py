@@ -118,7 +118,7 @@ def test_exact_ties_follow_tie_break():
 
 
 def test_large_logits_are_stable():
-    """Keys x 100 push logits to about +-1000: the two-pass softmax must
+    """Keys x 100 push logits to several hundred: the two-pass softmax must
     subtract row maxima (fp32 exp overflows past 88)."""
     wl = TINY.with_(name="big", wid=160, dtype="bf16", head_dim=128, k_mult=100.0, n_keys=3000, window=16,
                     kv_budget=200, n_hubs=0, hub_mode=None)
@@ -126,7 +126,7 @@ def test_large_logits_are_stable():
     inp = make_inputs(wl)
     gpu = run_gpu(wl, inp)
     ref = oracle_for(wl, inp)
-    assert np.abs(ref["lse"]).max() > 500
+    assert np.abs(ref["lse"]).max() > 300
     check_all(wl, inp, gpu, ref)
 
 
