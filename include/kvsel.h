@@ -116,7 +116,9 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
 kvsel_status_t kvsel_accumulate(int32_t batch, int32_t n_heads, int64_t n, const float* src, float* dst,
                                 int32_t mode, void* stream);
 
-/* Device workspace, in bytes, that kvsel_topk needs (0 on invalid sizes). */
+/* Device workspace, in bytes, that kvsel_topk needs (0 on invalid sizes): the
+ * per-chunk digit histograms, selection state and chunk counts of the
+ * multi-work-group radix select. */
 size_t kvsel_topk_workspace_bytes(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget);
 
 /*
@@ -131,7 +133,8 @@ size_t kvsel_topk_workspace_bytes(int32_t batch, int32_t rows, int64_t n_keys, i
  *         n_keys - 1; strictly ascending, window last.
  * The TSP token set calls this with rows = 1 on the head-mean score; the KV
  * set with rows = n_kv_heads.
- * Preconditions: 1 <= window <= budget <= n_keys < 2^31; batch * rows <= 2^31-1.
+ * workspace  device, >= kvsel_topk_workspace_bytes(...) bytes, 256-byte aligned.
+ * Preconditions: 1 <= window <= budget <= n_keys < 2^31; batch * rows <= 65535.
  * Errors: INVALID_ARG, WORKSPACE, HIP.
  */
 kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,

@@ -161,3 +161,11 @@ def test_accumulate_rejects(lib):
 
 def test_rate_helper():
     assert kvsel.budget_from_rate(0.1, 32768, 32) == 3277
+
+
+def test_topk_workspace_contract(lib):
+    need = lib.kvsel_topk_workspace_bytes(1, 8, 131072, 32, 4096)
+    assert need > 0 and lib.kvsel_topk_workspace_bytes(1, 8, 131072, 32, 4097 + 131072) == 0
+    assert lib.kvsel_topk(1, 8, 131072, 32, 4096, FAKE, FAKE, None, need, None) == 3
+    assert lib.kvsel_topk(1, 8, 131072, 32, 4096, FAKE, FAKE, FAKE, need - 1, None) == 3
+    assert lib.kvsel_topk(1, 8, 131072, 32, 4096, FAKE, FAKE, FAKE + 16, need, None) == 3

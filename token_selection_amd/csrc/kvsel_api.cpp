@@ -75,6 +75,36 @@ void make_geom(const kvsel_score_desc_t* d, ScoreGeom& g, int& RB) {
 
 ScoreWs ws_layout(const ScoreGeom& g) { return kvsel::score_workspace_layout(g.S, g.n_chunks1, g.Rpad, g.Np); }
 
+// Compute units of the current device; 256 (MI355X) when no device answers,
+// so that workspace queries also work on a host without a GPU.
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return n;
+}
+
+struct Plan {
+    ScoreGeom g;
+    int RB;
+    ScoreWs gen;       // general two-pass layout
+    kvsel::KresPlan kres;  // register-resident layout (kres.ok when eligible)
+    size_t total;
+};
+
+void make_plan(const kvsel_score_desc_t* d, Plan& p) {
+    make_geom(d, p.g, p.RB);
+    p.gen = ws_layout(p.g);
+    p.total = p.gen.total;
+    if (kvsel::kres_plan(d->dtype, d->head_dim, p.g.R, p.g.N, p.g.S, device_cu_count(), p.kres)) {
+        p.kres.total = p.kres.raw_off + (((size_t)p.g.S * p.g.Np * sizeof(float) + 255) & ~(size_t)255);
+        if (p.kres.total > p.total) p.total = p.kres.total;
+    }
+}
+
 kvsel_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
 
 }  // namespace
@@ -96,10 +126,9 @@ const char* kvsel_version(void) { return "kvsel 0.1.0 (gfx950)"; }
 
 size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc) {
     if (validate_desc(desc) != KVSEL_OK) return 0;
-    ScoreGeom g;
-    int RB;
-    make_geom(desc, g, RB);
-    return ws_layout(g).total;
+    Plan p;
+    make_plan(desc, p);
+    return p.total;
 }
 
 kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
@@ -109,20 +138,66 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
     if (st != KVSEL_OK) return st;
     if (!q_win || !k || !aligned16(q_win) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
     if (desc->n_keys > desc->window && !scores) return KVSEL_ERR_INVALID_ARG;
-    ScoreGeom g;
-    int RB;
-    make_geom(desc, g, RB);
-    const ScoreWs lay = ws_layout(g);
-    if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
+    Plan p;
+    make_plan(desc, p);
+    if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    ScoreGeom& g = p.g;
     g.q = q_win;
     g.k = k;
-    g.part = reinterpret_cast<float2*>(ws + lay.part_off);
-    g.lse2 = reinterpret_cast<float*>(ws + lay.lse2_off);
-    g.raw = reinterpret_cast<float*>(ws + lay.raw_off);
     g.lse_out = lse_out;
-    return from_hip(kvsel::launch_score(g, desc->dtype, desc->head_dim, RB, scores, accumulate ? 1 : 0,
-                                        desc->pool_kernel, static_cast<hipStream_t>(stream)));
+    float* raw = nullptr;
+    bool done = false;
+    if (p.kres.ok && kvsel::kres_fits(p.kres)) {
+        kvsel::KresArgs a;
+        a.q = static_cast<const uint16_t*>(q_win);
+        a.k = static_cast<const uint16_t*>(k);
+        for (int i = 0; i < 4; ++i) {
+            a.qs[i] = g.qs[i];
+            a.ks[i] = g.ks[i];
+        }
+        a.B = g.B;
+        a.Hq = g.Hq;
+        a.Hkv = g.Hkv;
+        a.G = g.G;
+        a.w = g.w;
+        a.R = g.R;
+        a.rbn = p.kres.rbn;
+        a.N = (int32_t)g.N;
+        a.Np = (int32_t)g.Np;
+        a.S = g.S;
+        a.team_wgs = p.kres.team_wgs;
+        a.n_teams = p.kres.n_teams;
+        a.n_act = p.kres.n_act;
+        a.wg_per_stream = p.kres.wg_per_stream;
+        a.c = g.c;
+        a.invG = g.invG;
+        a.part = reinterpret_cast<uint64_t*>(ws + p.kres.part_off);
+        a.lse2 = reinterpret_cast<float*>(ws + p.kres.lse2_off);
+        a.slots = reinterpret_cast<uint64_t*>(ws + p.kres.part_off);
+        a.n_slots = (int64_t)((p.kres.slots_end - p.kres.part_off) / sizeof(uint64_t));
+        a.abort_word = reinterpret_cast<uint32_t*>(ws + p.kres.abort_off);
+        a.raw = reinterpret_cast<float*>(ws + p.kres.raw_off);
+        a.lse_out = lse_out;
+        a.spin_limit = 100000000;  // 1 s of the 100 MHz wall clock
+        if (kvsel::launch_kres(p.kres, a, hs) == hipSuccess) {
+            raw = a.raw;
+            done = true;
+        } else {
+            (void)hipGetLastError();  // launch refused: use the general path
+        }
+    }
+    if (!done) {
+        g.part = reinterpret_cast<float2*>(ws + p.gen.part_off);
+        g.lse2 = reinterpret_cast<float*>(ws + p.gen.lse2_off);
+        g.raw = reinterpret_cast<float*>(ws + p.gen.raw_off);
+        const hipError_t e = kvsel::launch_score_passes(g, desc->dtype, desc->head_dim, p.RB, hs);
+        if (e != hipSuccess) return KVSEL_ERR_HIP;
+        raw = g.raw;
+    }
+    return from_hip(kvsel::launch_pool(raw, scores, g.L, (int64_t)g.B * g.Hkv, g.Np, desc->pool_kernel,
+                                       accumulate ? 1 : 0, hs));
 }
 
 kvsel_status_t kvsel_accumulate(int32_t batch, int32_t n_heads, int64_t n, const float* src, float* dst,
@@ -133,23 +208,20 @@ kvsel_status_t kvsel_accumulate(int32_t batch, int32_t n_heads, int64_t n, const
 }
 
 size_t kvsel_topk_workspace_bytes(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget) {
-    (void)batch;
-    (void)rows;
-    (void)n_keys;
-    (void)window;
-    (void)budget;
-    return 0;  // the single-work-group-per-row select keeps its state in LDS
+    if (batch < 1 || rows < 1 || (int64_t)batch * rows > 65535) return 0;
+    if (window < 1 || budget < window || n_keys < budget || n_keys >= kMaxKeys) return 0;
+    return kvsel::topk_workspace_bytes(batch * rows, n_keys - window);
 }
 
 kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
                           const float* scores, int32_t* idx, void* workspace, size_t workspace_bytes,
                           void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
-    if (batch < 1 || rows < 1 || (int64_t)batch * rows > INT32_MAX) return KVSEL_ERR_INVALID_ARG;
+    if (batch < 1 || rows < 1 || (int64_t)batch * rows > 65535) return KVSEL_ERR_INVALID_ARG;
     if (window < 1 || budget < window || n_keys < budget || n_keys >= kMaxKeys) return KVSEL_ERR_INVALID_ARG;
     if (!idx || (n_keys > window && !scores)) return KVSEL_ERR_INVALID_ARG;
-    return from_hip(kvsel::launch_topk(batch * rows, n_keys, window, budget, scores, idx,
+    const size_t need = kvsel::topk_workspace_bytes(batch * rows, n_keys - window);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
+    return from_hip(kvsel::launch_topk(batch * rows, n_keys, window, budget, scores, idx, workspace,
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -39,14 +39,53 @@ constexpr int kScoreChunk = 1024;  // keys per work-group in both passes
 int score_row_blocks(int dtype, int head_dim, int R);  // RB (row blocks of 16 per group)
 ScoreWs score_workspace_layout(int64_t S, int64_t n_chunks1, int64_t Rpad, int64_t Np);
 
-hipError_t launch_score(const ScoreGeom& g, int dtype, int head_dim, int RB, float* scores, int accumulate,
-                        int pool_kernel, hipStream_t stream);
+// General path: two launches over K (LSE partials + combine, then scores).
+hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int RB, hipStream_t stream);
+
+// Average pool of raw [L][B*Hkv][Np], summed over layers, written or added to scores.
+hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64_t Np, int pool_kernel,
+                       int accumulate, hipStream_t stream);
+
+// Register-resident path (bf16): one cooperative launch reads K once.
+struct KresArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    int64_t qs[4];
+    int64_t ks[4];
+    int32_t B, Hq, Hkv, G, w, R, rbn;
+    int32_t N, Np, S;
+    int32_t team_wgs;       // work-groups that split one slab's keys
+    int32_t n_teams;        // teams per stream
+    int32_t n_act;          // work-groups of a team that hold keys
+    int32_t wg_per_stream;  // n_teams * team_wgs; the grid is two streams
+    float c, invG;
+    uint64_t* part;   // [S][team_wgs][rp] per-work-group (max, sum) bit pairs, log2 domain
+    float* lse2;      // [S][rp] row LSE, log2 domain (directly after part)
+    uint64_t* slots;  // part and lse2 as one span of n_slots 64-bit words (sentinel-filled)
+    int64_t n_slots;
+    uint32_t* abort_word;
+    float* raw;       // [S][Np]
+    float* lse_out;   // [L][B][Hq][w] or null
+    int64_t spin_limit;  // wall-clock ticks (100 MHz) a wait may last
+};
+
+struct KresPlan {
+    bool ok;
+    int head_dim;
+    int kb, team_wgs, n_teams, n_act, wg_per_stream, rbn, rbn_cap, rp;
+    size_t part_off, lse2_off, slots_end, abort_off, raw_off, total;
+};
+
+bool kres_plan(int dtype, int head_dim, int R, int64_t N, int64_t S, int n_cu, KresPlan& plan);
+bool kres_fits(const KresPlan& plan);
+hipError_t launch_kres(const KresPlan& plan, KresArgs a, hipStream_t stream);
 
 hipError_t launch_accumulate(int32_t B, int32_t H, int64_t n, const float* src, float* dst, int mode,
                              hipStream_t stream);
 
+size_t topk_workspace_bytes(int32_t rows, int64_t n_prefix);
 hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, const float* scores,
-                       int32_t* idx, hipStream_t stream);
+                       int32_t* idx, void* workspace, hipStream_t stream);
 
 hipError_t launch_gather(int32_t L, int32_t B, int32_t H, int32_t idx_heads, int32_t budget, int64_t n_src_rows,
                          int64_t row_bytes, const void* src, const int64_t s[4], const int32_t* idx, void* dst,

@@ -301,27 +301,46 @@ __global__ __launch_bounds__(256) void raw_score_kernel(ScoreGeom g) {
     }
 }
 
-// Average pool (zero padded, divisor = kernel) of every layer's raw scores,
-// summed over layers in layer order, added to scores when accumulating.
+// Average pool (zero padded, divisor = kernel) of the raw scores summed over
+// the layers of the call, added to scores when accumulating. Pooling is
+// linear, so the layers are summed first and pooled once: each work-group
+// sums a 256-position tile plus a halo of r positions on each side, with
+// every layer's load issued before the first add, then pools from LDS.
+constexpr int kPoolTile = 256;
+constexpr int kPoolMaxR = 127;
 __global__ __launch_bounds__(256) void pool_acc_kernel(const float* __restrict__ raw, float* __restrict__ scores,
                                                        int L, int64_t BH, int64_t Np, int kern, int accumulate) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= BH * Np) return;
-    const int64_t bh = idx / Np;
-    const int64_t j = idx - bh * Np;
+    __shared__ float tile[kPoolTile + 2 * kPoolMaxR];
+    const int64_t bh = blockIdx.y;
+    const int64_t j0 = (int64_t)blockIdx.x * kPoolTile;
     const int r = (kern - 1) / 2;
-    const float inv_div = (float)kern;
-    float acc = accumulate ? scores[idx] : 0.f;
-    for (int l = 0; l < L; ++l) {
-        const float* rr = raw + ((int64_t)l * BH + bh) * Np;
+    const int span = kPoolTile + 2 * r;
+    for (int t = threadIdx.x; t < span; t += 256) {
+        const int64_t j = j0 - r + t;
         float sum = 0.f;
-        for (int t = -r; t <= r; ++t) {
-            const int64_t jj = j + t;
-            if (jj >= 0 && jj < Np) sum += rr[jj];
+        if (j >= 0 && j < Np) {
+            const float* p = raw + bh * Np + j;
+            const int64_t lstride = BH * Np;
+            int l = 0;
+            for (; l + 8 <= L; l += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(l + u) * lstride];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) sum += v[u];
+            }
+            for (; l < L; ++l) sum += p[(int64_t)l * lstride];
         }
-        acc += sum / inv_div;
+        tile[t] = sum;
     }
-    scores[idx] = acc;
+    __syncthreads();
+    const int64_t j = j0 + threadIdx.x;
+    if (j >= Np) return;
+    float pooled = 0.f;
+    for (int t = 0; t < kern; ++t) pooled += tile[threadIdx.x + t];
+    const float val = pooled / (float)kern;
+    const int64_t o = bh * Np + j;
+    scores[o] = accumulate ? scores[o] + val : val;
 }
 
 template <typename T, int D, int RB>
@@ -381,8 +400,7 @@ ScoreWs score_workspace_layout(int64_t S, int64_t n_chunks1, int64_t Rpad, int64
     return w;
 }
 
-hipError_t launch_score(const ScoreGeom& g, int dtype, int head_dim, int RB, float* scores, int accumulate,
-                        int pool_kernel, hipStream_t st) {
+hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int RB, hipStream_t st) {
     bool ok = false;
     if (dtype == KVSEL_DTYPE_BF16) {
         ok = head_dim == 128 ? dispatch_rb<uint16_t, 128>(g, RB, st) : dispatch_rb<uint16_t, 64>(g, RB, st);
@@ -390,12 +408,15 @@ hipError_t launch_score(const ScoreGeom& g, int dtype, int head_dim, int RB, flo
         ok = head_dim == 128 ? dispatch_rb<float, 128>(g, RB, st) : dispatch_rb<float, 64>(g, RB, st);
     }
     if (!ok) return hipErrorInvalidValue;
-    if (g.Np > 0) {
-        const int64_t BH = (int64_t)g.B * g.Hkv;
-        const int64_t total = BH * g.Np;
-        hipLaunchKernelGGL(pool_acc_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, g.raw, scores,
-                           g.L, BH, g.Np, pool_kernel, accumulate);
-    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64_t Np, int pool_kernel,
+                       int accumulate, hipStream_t st) {
+    if (Np <= 0) return hipSuccess;
+    if ((pool_kernel - 1) / 2 > kPoolMaxR || BH > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pool_acc_kernel, dim3((unsigned)((Np + kPoolTile - 1) / kPoolTile), (unsigned)BH), dim3(256), 0,
+                       st, raw, scores, L, BH, Np, pool_kernel, accumulate);
     return hipGetLastError();
 }
 

@@ -4,14 +4,23 @@
 // newest; the budgets for the propagated token set and for the stored KV
 // entries are separate calls (FastKV section 2B, StructKV section 3).
 //
-// Selection is exact and deterministic: the k-th largest score is found by a
-// most-significant-digit-first radix select over the order-preserving
-// integer image of the fp32 score bits (four 8-bit digits, histograms in
-// LDS), which yields the threshold T and how many of the elements equal to T
-// are taken. A block-wide scan then writes, in ascending position, every
-// element above T and the lowest-positioned elements equal to T - which is
-// exactly the order "score descending, then position ascending". The window
-// positions follow.
+// Selection is exact and deterministic. Scores map to an order-preserving
+// 32-bit key; the k-th largest key T is found by a most-significant-digit
+// radix select (digits of 11, 11 and 10 bits), which also yields how many
+// keys equal to T are kept. Writing, in ascending position, every key above
+// T and the lowest-positioned keys equal to T gives exactly the order "score
+// descending, then position ascending"; the window positions follow.
+//
+// Every row is split into chunks handled by separate work-groups so that a
+// handful of rows still fills the chip. Kernel boundaries order the steps:
+//   hist(p)   per chunk: LDS histogram of digit p over keys matching the
+//             prefix chosen so far, added bin by bin (integer atomics, so the
+//             total is exact and order-independent) into hist[row][p][bins]
+//   select(p) per row: suffix-scan the bins, pick the digit holding the k-th
+//             key, update (prefix, remaining)
+//   count     per chunk: keys above T and equal to T
+//   write     per chunk: exclusive offsets from the earlier chunks' counts,
+//             then an in-order block scan that writes kept positions.
 
 #include <stdint.h>
 
@@ -20,15 +29,72 @@
 namespace kvsel {
 namespace {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkPerThread = 4;
-constexpr int kTopkTile = kTopkThreads * kTopkPerThread;
+constexpr int kThreads = 256;
+constexpr int kBins = 2048;  // 11-bit digits
+constexpr int kPasses = 3;
+__host__ __device__ constexpr int digit_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
+__host__ __device__ constexpr uint32_t digit_mask(int p) { return p == 2 ? 0x3FFu : 0x7FFu; }
+// key bits already decided before pass p
+__host__ __device__ constexpr uint32_t prefix_mask(int p) {
+    return p == 0 ? 0u : (p == 1 ? 0xFFE00000u : 0xFFFFFC00u);
+}
 
 // Monotone map from fp32 bits to uint32: a < b (as floats) <=> key(a) < key(b);
 // -0 ranks equal to +0.
 __device__ __forceinline__ uint32_t order_key(uint32_t u) {
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct TopkGeom {
+    const uint32_t* x;  // scores as bits [rows][Np]
+    int32_t* idx;       // [rows][budget]
+    int64_t Np;
+    int32_t w, budget, kk;
+    int32_t chunks;     // chunks per row
+    int64_t chunk_len;  // elements per chunk (the last one may be shorter)
+    uint32_t* hist;     // [rows][kPasses][kBins], zeroed by the window kernel
+    uint32_t* state;    // [rows][2]: prefix, remaining
+    uint32_t* counts;   // [rows][chunks][2]: keys above T, keys equal to T
+};
+
+__device__ __forceinline__ void chunk_range(const TopkGeom& g, int chunk, int64_t& b, int64_t& e) {
+    b = (int64_t)chunk * g.chunk_len;
+    e = b + g.chunk_len;
+    if (e > g.Np) e = g.Np;
+    if (b > g.Np) b = g.Np;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkGeom g, int pass) {
+    __shared__ uint32_t h[kBins];
+    const int chunk = blockIdx.x;
+    const int64_t row = blockIdx.y;
+    for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
+    const uint32_t prefix = pass == 0 ? 0u : g.state[row * 2];
+    const uint32_t pm = prefix_mask(pass);
+    const int shift = digit_shift(pass);
+    const uint32_t dm = digit_mask(pass);
+    __syncthreads();
+    int64_t b, e;
+    chunk_range(g, chunk, b, e);
+    const uint32_t* x = g.x + row * g.Np;
+    for (int64_t i0 = b; i0 < e; i0 += kThreads * 8) {
+        uint32_t u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t i = i0 + threadIdx.x + (int64_t)k * kThreads;
+            u[k] = i < e ? order_key(x[i]) : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t i = i0 + threadIdx.x + (int64_t)k * kThreads;
+            if (i < e && (u[k] & pm) == prefix) atomicAdd(&h[(u[k] >> shift) & dm], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t* out = g.hist + (row * kPasses + pass) * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kThreads)
+        if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
@@ -40,110 +106,255 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
     return v;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(const float* __restrict__ scores,
-                                                               int32_t* __restrict__ idx, int64_t Np, int32_t w,
-                                                               int32_t budget) {
+// One work-group per row: scan the merged histogram of pass p and choose
+// the digit that holds the k-th largest key among those still matching.
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(TopkGeom g, int pass) {
+    constexpr int PER = kBins / kThreads;  // 8 consecutive digits per thread, highest first
+    __shared__ uint32_t wsum[kThreads / 64];
     const int64_t row = blockIdx.x;
-    const uint32_t* x = reinterpret_cast<const uint32_t*>(scores) + row * Np;
-    int32_t* out = idx + row * (int64_t)budget;
-    const int32_t kk = budget - w;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sh[2];
-    __shared__ uint32_t wsum[kTopkThreads / 64];
-
-    if (kk > 0) {
-        uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)kk;
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            if (tid < 256) hist[tid] = 0u;
-            __syncthreads();
-            for (int64_t i = tid; i < Np; i += kTopkThreads) {
-                const uint32_t u = order_key(x[i]);
-                if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 0xFFu], 1u);
-            }
-            __syncthreads();
-            if (tid == 0) {
-                // walk digits from the top until the running count reaches
-                // the number still to be selected
-                uint32_t cum = 0u;
-                int dgt = 255;
-                for (; dgt > 0; --dgt) {
-                    const uint32_t c = hist[dgt];
-                    if (cum + c >= remaining) break;
-                    cum += c;
-                }
-                sh[0] = prefix | ((uint32_t)dgt << shift);
-                sh[1] = remaining - cum;
-            }
-            __syncthreads();
-            prefix = sh[0];
-            remaining = sh[1];
-            mask |= 0xFFu << shift;
-            __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t prefix = pass == 0 ? 0u : g.state[row * 2];
+    const uint32_t remaining = pass == 0 ? (uint32_t)g.kk : g.state[row * 2 + 1];
+    uint32_t c[PER];
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int d = kBins - 1 - (tid * PER + k);
+        c[k] = g.hist[(row * kPasses + pass) * kBins + d];
+        tot += c[k];
+    }
+    const uint32_t incl = wave_inclusive_scan(tot, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t above = incl - tot;  // keys in digits above this thread's first digit
+    for (int w2 = 0; w2 < wave; ++w2) above += wsum[w2];
+    __syncthreads();  // every thread has read the state before it changes
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int d = kBins - 1 - (tid * PER + k);
+        if (above < remaining && above + c[k] >= remaining) {
+            g.state[row * 2] = prefix | ((uint32_t)d << digit_shift(pass));
+            g.state[row * 2 + 1] = remaining - above;
         }
-        const uint32_t T = prefix;         // key of the kk-th largest score
-        const uint32_t take_eq = remaining;  // how many elements equal to T are kept
-        uint32_t base_gt = 0u, base_eq = 0u;
-        for (int64_t t0 = 0; t0 < Np; t0 += kTopkTile) {
-            uint32_t flags = 0u, cgt = 0u, ceq = 0u;
+        above += c[k];
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_count_kernel(TopkGeom g) {
+    __shared__ uint32_t red[2][kThreads / 64];
+    const int chunk = blockIdx.x;
+    const int64_t row = blockIdx.y;
+    const uint32_t T = g.state[row * 2];
+    int64_t b, e;
+    chunk_range(g, chunk, b, e);
+    const uint32_t* x = g.x + row * g.Np;
+    uint32_t gt = 0u, eq = 0u;
+    for (int64_t i0 = b; i0 < e; i0 += kThreads * 8) {
+        uint32_t u[8];
 #pragma unroll
-            for (int e = 0; e < kTopkPerThread; ++e) {
-                const int64_t i = t0 + (int64_t)tid * kTopkPerThread + e;
-                if (i < Np) {
-                    const uint32_t u = order_key(x[i]);
-                    if (u > T) {
-                        flags |= 1u << e;
-                        ++cgt;
-                    } else if (u == T) {
-                        flags |= 16u << e;
-                        ++ceq;
-                    }
-                }
+        for (int k = 0; k < 8; ++k) {
+            const int64_t i = i0 + threadIdx.x + (int64_t)k * kThreads;
+            u[k] = i < e ? order_key(x[i]) : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t i = i0 + threadIdx.x + (int64_t)k * kThreads;
+            gt += (i < e && u[k] > T) ? 1u : 0u;
+            eq += (i < e && u[k] == T) ? 1u : 0u;
+        }
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        gt += __shfl_xor(gt, off);
+        eq += __shfl_xor(eq, off);
+    }
+    if (lane == 0) {
+        red[0][wave] = gt;
+        red[1][wave] = eq;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t sg = 0u, se = 0u;
+        for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+            sg += red[0][w2];
+            se += red[1][w2];
+        }
+        g.counts[(row * g.chunks + chunk) * 2] = sg;
+        g.counts[(row * g.chunks + chunk) * 2 + 1] = se;
+    }
+}
+
+// Write this chunk's kept positions in ascending order: a key above T is
+// kept; a key equal to T is kept while fewer than take_eq equal keys precede
+// it in the row. The output slot is (#keys above T before it) +
+// min(#equal keys before it, take_eq).
+__global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkGeom g) {
+    constexpr int PER = 16;  // consecutive elements per thread per tile
+    __shared__ uint32_t wsum[kThreads / 64];
+    __shared__ uint32_t wsum2[kThreads / 64];
+    __shared__ uint32_t base_sh[2];
+    const int chunk = blockIdx.x;
+    const int64_t row = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t T = g.state[row * 2];
+    const uint32_t take_eq = g.state[row * 2 + 1];
+    int32_t* out = g.idx + row * (int64_t)g.budget;
+    {
+        // counts of the chunks before this one, summed by the whole block
+        uint32_t sg = 0u, se = 0u;
+        for (int ch = tid; ch < chunk; ch += kThreads) {
+            sg += g.counts[(row * g.chunks + ch) * 2];
+            se += g.counts[(row * g.chunks + ch) * 2 + 1];
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            sg += __shfl_xor(sg, off);
+            se += __shfl_xor(se, off);
+        }
+        if (lane == 0) {
+            wsum[wave] = sg;
+            wsum2[wave] = se;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t a0 = 0u, a1 = 0u;
+            for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+                a0 += wsum[w2];
+                a1 += wsum2[w2];
             }
-            // block exclusive scan of (gt count, eq count) packed 16:16; a
-            // tile holds at most 4096 elements so neither half overflows
-            const uint32_t v = (cgt << 16) | ceq;
-            const uint32_t incl = wave_inclusive_scan(v, lane);
-            if (lane == 63) wsum[wave] = incl;
-            __syncthreads();
-            uint32_t before = 0u, total = 0u;
+            base_sh[0] = a0;
+            base_sh[1] = a1;
+        }
+    }
+    __syncthreads();
+    uint32_t base_gt = base_sh[0], base_eq = base_sh[1];
+    int64_t b, e;
+    chunk_range(g, chunk, b, e);
+    const uint32_t* x = g.x + row * g.Np;
+    for (int64_t t0 = b; t0 < e; t0 += (int64_t)kThreads * PER) {
+        uint32_t u[PER];
+        const int64_t first = t0 + (int64_t)tid * PER;
 #pragma unroll
-            for (int w2 = 0; w2 < kTopkThreads / 64; ++w2) {
-                const uint32_t s = wsum[w2];
-                if (w2 < wave) before += s;
-                total += s;
-            }
-            const uint32_t excl = before + incl - v;
-            uint32_t gt_before = base_gt + (excl >> 16);
-            uint32_t eq_before = base_eq + (excl & 0xFFFFu);
+        for (int k = 0; k < PER; ++k) u[k] = first + k < e ? order_key(x[first + k]) : 0u;
+        uint32_t cgt = 0u, ceq = 0u;
 #pragma unroll
-            for (int e = 0; e < kTopkPerThread; ++e) {
-                const int32_t i = (int32_t)(t0 + (int64_t)tid * kTopkPerThread + e);
-                if (flags & (1u << e)) {
+        for (int k = 0; k < PER; ++k) {
+            const bool in = first + k < e;
+            cgt += (in && u[k] > T) ? 1u : 0u;
+            ceq += (in && u[k] == T) ? 1u : 0u;
+        }
+        // packed 16:16 block scan; a tile holds 4096 elements
+        const uint32_t v = (cgt << 16) | ceq;
+        const uint32_t incl = wave_inclusive_scan(v, lane);
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        uint32_t before = 0u, total = 0u;
+#pragma unroll
+        for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+            const uint32_t s2 = wsum[w2];
+            if (w2 < wave) before += s2;
+            total += s2;
+        }
+        const uint32_t excl = before + incl - v;
+        uint32_t gt_before = base_gt + (excl >> 16);
+        uint32_t eq_before = base_eq + (excl & 0xFFFFu);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            if (first + k < e) {
+                const int32_t i = (int32_t)(first + k);
+                if (u[k] > T) {
                     out[gt_before + min(eq_before, take_eq)] = i;
                     ++gt_before;
-                } else if (flags & (16u << e)) {
+                } else if (u[k] == T) {
                     if (eq_before < take_eq) out[gt_before + eq_before] = i;
                     ++eq_before;
                 }
             }
-            base_gt += total >> 16;
-            base_eq += total & 0xFFFFu;
-            __syncthreads();
         }
+        base_gt += total >> 16;
+        base_eq += total & 0xFFFFu;
+        __syncthreads();
     }
-    for (int32_t m = tid; m < w; m += kTopkThreads) out[kk + m] = (int32_t)Np + m;
 }
+
+// Writes the window positions and zeroes the digit histograms (it runs first).
+__global__ __launch_bounds__(kThreads) void topk_window_kernel(int32_t* idx, int32_t rows, int64_t Np, int32_t w,
+                                                               int32_t budget, uint32_t* hist) {
+    if (hist) {
+        const int64_t nh = (int64_t)rows * kPasses * kBins;
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nh; i += (int64_t)gridDim.x * kThreads)
+            hist[i] = 0u;
+    }
+    const int64_t total = (int64_t)rows * w;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t row = i / w;
+        const int32_t m = (int32_t)(i - row * w);
+        idx[row * budget + (budget - w) + m] = (int32_t)Np + m;
+    }
+}
+
+void plan_chunks(int32_t rows, int64_t Np, int32_t& chunks, int64_t& chunk_len) {
+    // about 512 work-groups in all, each with at least 2048 elements
+    int64_t c = (512 + rows - 1) / rows;
+    const int64_t max_c = (Np + 2047) / 2048;
+    if (c > max_c) c = max_c;
+    if (c < 1) c = 1;
+    chunk_len = (Np + c - 1) / c;
+    chunk_len = (chunk_len + 255) & ~(int64_t)255;
+    if (chunk_len < 256) chunk_len = 256;
+    chunks = (int32_t)((Np + chunk_len - 1) / chunk_len);
+    if (chunks < 1) chunks = 1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+size_t topk_workspace_bytes(int32_t rows, int64_t Np) {
+    int32_t chunks;
+    int64_t chunk_len;
+    plan_chunks(rows, Np > 0 ? Np : 1, chunks, chunk_len);
+    return align256((size_t)rows * kPasses * kBins * sizeof(uint32_t)) + align256((size_t)rows * 2 * sizeof(uint32_t)) +
+           align256((size_t)rows * chunks * 2 * sizeof(uint32_t));
+}
+
 hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, const float* scores,
-                       int32_t* idx, hipStream_t st) {
+                       int32_t* idx, void* ws, hipStream_t st) {
     const int64_t Np = n_keys - window;
-    hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kTopkThreads), 0, st, scores, idx, Np, window, budget);
+    TopkGeom g;
+    g.x = reinterpret_cast<const uint32_t*>(scores);
+    g.idx = idx;
+    g.Np = Np;
+    g.w = window;
+    g.budget = budget;
+    g.kk = budget - window;
+    g.hist = nullptr;
+    if (g.kk > 0) {
+        plan_chunks(rows, Np, g.chunks, g.chunk_len);
+        char* p = static_cast<char*>(ws);
+        g.hist = reinterpret_cast<uint32_t*>(p);
+        p += align256((size_t)rows * kPasses * kBins * sizeof(uint32_t));
+        g.state = reinterpret_cast<uint32_t*>(p);
+        p += align256((size_t)rows * 2 * sizeof(uint32_t));
+        g.counts = reinterpret_cast<uint32_t*>(p);
+    }
+    int64_t work = (int64_t)rows * window;
+    if (g.hist && (int64_t)rows * kPasses * kBins > work) work = (int64_t)rows * kPasses * kBins;
+    int64_t blocks = (work + kThreads - 1) / kThreads;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(topk_window_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, idx, rows, Np, window, budget,
+                       g.hist);
+    if (g.kk > 0) {
+        const dim3 grid((unsigned)g.chunks, (unsigned)rows);
+        for (int pass = 0; pass < kPasses; ++pass) {
+            hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, st, g, pass);
+            hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, g, pass);
+        }
+        hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, st, g);
+        hipLaunchKernelGGL(topk_write_kernel, grid, dim3(kThreads), 0, st, g);
+    }
     return hipGetLastError();
 }
 
