@@ -23,6 +23,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def recorded_traffic(kernel: str, source: str):
+    """HBM bytes per launch of `kernel` from the rocprofv3 PMC summaries under
+    profiles/, if they were taken on the current source of that kernel
+    (matching sha256); otherwise None."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, source)
+    if not os.path.exists(path) or not os.path.isdir(PROFILES):
+        return None
+    sha = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    pat = re.compile(r"traffic: kernel=(\S+) source=(\S+) sha256=([0-9a-f]+) bytes_per_launch=(\d+)")
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith(".md"):
+            continue
+        for m in pat.finditer(open(os.path.join(PROFILES, name)).read()):
+            if m.group(1) == kernel and m.group(2) == source and m.group(3) == sha:
+                return int(m.group(4))
+    return None
 
 
 def _cores() -> int:
@@ -67,6 +89,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="structkv_128k_16l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer 3 times (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for --gpus {args.gpus})",
@@ -75,6 +99,15 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
+        return 0
 
     from token_selection_amd import kvsel as K
     from workloads import get_workload, make_inputs
@@ -171,8 +204,12 @@ def main() -> int:
         "hbm_gbs_whole_path": whole_gbs,
         "hbm_frac_whole_path": whole_gbs / HBM_PEAK_GBS,
         "stage_ms": stage_ms,
-        "roofline": {"bound": "hbm", "kernel": "kvsel_score", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        # dominant kernel: kres_kernel (with its sentinel-fill and pool launches,
+        # together kvsel_score); algorithmic bytes = K read once + Q + scores
+        "roofline": {"bound": "hbm", "kernel": "kres_kernel (kvsel_score)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic("kres_kernel", "token_selection_amd/csrc/kres.hip"),
+                     "algorithmic_bytes": score_alg_bytes},
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
     }
