@@ -14,16 +14,31 @@ pytestmark = pytest.mark.gpu
 THREADS = 16
 
 
+_CACHE = {}
+
+
+def inputs_and_oracle(name):
+    """Inputs and fp64 oracle results of a workload, computed once per session."""
+    if name not in _CACHE:
+        wl = get_workload(name)
+        t0 = time.time()
+        say(f"case {name}: generating inputs")
+        inp = make_inputs(wl, threads=THREADS)
+        say(f"case {name}: running the oracle ({time.time() - t0:.1f}s)")
+        ref = oracle_for(wl, inp, threads=THREADS)
+        _CACHE.clear()  # keep one workload's arrays at a time
+        _CACHE[name] = (wl, inp, ref)
+    return _CACHE[name]
+
+
+@pytest.mark.parametrize("path", ["stream", "resident"])
 @pytest.mark.parametrize("name", ["llama8b_32k_tsp", "batched_8x32k_ar1", "qwen7b_512k", "structkv_128k_16l"])
-def test_full_workload(name):
-    wl = get_workload(name)
+def test_full_workload(path, name, monkeypatch):
+    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
+    wl, inp, ref = inputs_and_oracle(name)
     t0 = time.time()
-    say(f"case {name}: generating inputs")
-    inp = make_inputs(wl, threads=THREADS)
-    say(f"case {name}: running the HIP path ({time.time() - t0:.1f}s)")
+    say(f"case {name} [{path}]: running the HIP path")
     gpu = run_gpu(wl, inp)
-    say(f"case {name}: running the oracle ({time.time() - t0:.1f}s)")
-    ref = oracle_for(wl, inp, threads=THREADS)
-    say(f"case {name}: comparing ({time.time() - t0:.1f}s)")
+    say(f"case {name} [{path}]: comparing ({time.time() - t0:.1f}s)")
     check_all(wl, inp, gpu, ref)
-    say(f"case {name}: done ({time.time() - t0:.1f}s)")
+    say(f"case {name} [{path}]: done ({time.time() - t0:.1f}s)")

@@ -47,10 +47,14 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("path", ["stream", "resident", "general"])
 @pytest.mark.parametrize("case", RAGGED, ids=lambda c: "-".join(map(str, c)))
-def test_ragged_shapes(case):
+def test_ragged_shapes(case, path, monkeypatch):
+    """Every scoring path the library has (where a shape is outside a path's
+    range the library takes the next one, so those cases repeat a path)."""
     dt, L, B, Hq, Hkv, d, N, w, pool, budget = case
-    say("case ragged", case)
+    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
+    say("case ragged", case, path)
     wl = TINY.with_(name="ragged", wid=100 + RAGGED.index(case), dtype=dt, n_layers=L, batch=B, n_q_heads=Hq,
                     n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool, kv_budget=budget,
                     n_hubs=min(8, max(0, N - w - 1)))

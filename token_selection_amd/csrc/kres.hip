@@ -10,8 +10,8 @@
 //
 // One slab, seen from one work-group of its team:
 //   1. stage the slab's G*w query rows in LDS; load its key range into VGPRs;
-//   2. pass 1: logits on v_mfma_f32_16x16x32_bf16, (max, sum of exp2) per
-//      row over its keys, merged to one partial per row and published;
+//   2. pass 1: logits on v_mfma_f32_32x32x16_bf16, (reference, sum of exp2)
+//      per row over its keys, merged to one partial per row and published;
 //   3. the owner of row r (work-group r mod team size) merges the team's
 //      partials of that row into the row's LSE and publishes it;
 //   4. every work-group reads all row LSEs, then pass 2 recomputes the
@@ -31,38 +31,29 @@
 // grid is sized to the occupancy the device reports, so every work-group of a
 // team is resident together.
 //
-// Operand layout (16x16x32 bf16): lane l supplies row/column (l % 16) and the
-// 8 consecutive k-slots of lane group (l / 16). At k-step ks the slot
-// (group, v) carries head-dim element ks*32 + group*8 + v, for K and Q alike,
-// so each key's four lanes read 64 contiguous bytes per load.
-
+// Operands use the 32x32x16 layout of tile32.h. Keys are read from HBM with
+// whole rows per load instruction and reshaped into that layout through a
+// per-wave LDS staging area: loading the fragments directly would touch a
+// cache line per lane and instruction.
+//
+// Within a wave the exponentials of one 32-key block are issued while the
+// matrix core computes the next block's logits, so the two units overlap.
 #include <math.h>
 #include <stdint.h>
 
 #include "kvsel.h"
 #include "kvsel_internal.h"
+#include "tile32.h"
 
 namespace kvsel {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kNegBig = -1.0e30f;
-
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+using namespace tile;
 
 constexpr uint64_t kEmpty64 = ~0ull;
 constexpr uint32_t kEmpty32 = ~0u;
 
 __device__ __forceinline__ uint32_t ld32(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st32(uint32_t* p, uint32_t v) {
@@ -91,83 +82,66 @@ __device__ bool poll(const T* p, T empty, T& v, uint32_t* abort_word, uint64_t t
     return true;
 }
 
-__device__ __forceinline__ void merge(float& m, float& z, float mo, float zo) {
-    const float mn = fmaxf(m, mo);
-    z = z * fexp2(m - mn) + zo * fexp2(mo - mn);
-    m = mn;
+// Dense index of the compute unit this wave runs on: XCC_ID and the SE / SH /
+// CU fields of HW_ID (hardware registers 20 and 4), kTurnKeys entries.
+constexpr int kTurnKeys = 2048;
+__device__ __forceinline__ uint32_t cu_key() {
+    const uint32_t hw = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11));
+    const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
+    return ((xcc & 7u) << 8) | (((hw >> 13) & 7u) << 5) | (((hw >> 12) & 1u) << 4) | ((hw >> 8) & 15u);
 }
 
-// Pass 1 on one 16-row block: logits of this lane's row against the wave's
-// KB*16 keys, reduced to a (reference, sum of exp2(x - reference)) pair.
-// Any logit of the row is a valid reference as far as the final LSE goes (the
-// merge rescales partials by their references); the maximum only has to keep
-// exp2 from overflowing. Away from the window the first logit is the
-// reference, so the exponentials can start while later products are still in
-// the matrix pipe; if some logit exceeds it by more than 2^64 the block is
-// redone with the maximum. Blocks that reach the causal window mask their
-// invisible keys and use the maximum directly.
-template <int D, int KB, bool EDGE>
-__device__ __forceinline__ void pass1_block(const bf16x8 (&kf)[KB][D / 32], const bf16x8 (&qf)[D / 32], float c,
-                                            int kfirst, int lim, float& m_out, float& z_out) {
-    constexpr int KS = D / 32;
-    f32x4 acc[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc[kb] = mma(kf[kb][ks], qf[ks], acc[kb]);
+// Load turns of the two work-groups sharing a CU (entry: presence of stream 0
+// and 1, loads completed by stream 0 and 1). Stream 0 issues its k-th slab's
+// key loads once stream 1 has completed k loads, stream 1 its k-th once stream
+// 0 has completed k+1, so the two streams' HBM phases alternate instead of
+// colliding. This only orders work: a wait that finds no partner, or lasts
+// longer than kTurnTicks, gives up and proceeds.
+constexpr uint64_t kTurnTicks = 5000;  // 50 us of the 100 MHz wall clock
+__device__ void turn_wait(uint32_t* tent, int p, int k, bool& solo) {
+    if (solo) return;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    if (p == 0) {
+        if (k == 0 || ld32(tent + 1) == 0u) return;
+        while (ld32(tent + 3) < (uint32_t)k) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kTurnTicks) return;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    } else {
+        for (;;) {
+            if (ld32(tent) != 0u && ld32(tent + 2) >= (uint32_t)(k + 1)) return;
+            const uint64_t dt = __builtin_amdgcn_s_memrealtime() - t0;
+            if (dt > kTurnTicks || (dt > kTurnTicks / 10 && ld32(tent) == 0u)) {
+                solo = ld32(tent) == 0u;  // no partner on this CU: stop waiting
+                return;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
     }
-    if (EDGE) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (kfirst + kb * 16 + v > lim) acc[kb][v] = -INFINITY;
-    }
-    float mxa = acc[0][0], mxb = acc[0][1];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        mxa = fmaxf(mxa, fmaxf(acc[kb][0], acc[kb][2]));
-        mxb = fmaxf(mxb, fmaxf(acc[kb][1], acc[kb][3]));
-    }
-    const float mx = fmaxf(mxa, mxb) * c;
-    float ref = EDGE ? fmaxf(kNegBig, mx) : acc[0][0] * c;
-    float zs[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) zs[v] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) zs[v] += fexp2(acc[kb][v] * c - ref);
-    if (!EDGE && __any(mx - ref > 64.f)) {
-        ref = fmaxf(ref, mx);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) zs[v] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) zs[v] += fexp2(acc[kb][v] * c - ref);
-    }
-    m_out = ref;
-    z_out = (zs[0] + zs[1]) + (zs[2] + zs[3]);
 }
+
 
 template <int D, int KB, int RBN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 kres_kernel(KresArgs a) {
-    constexpr int KS = D / 32;     // k-steps per fragment
-    constexpr int RP = RBN * 16;   // row capacity
+    constexpr int KS = D / 16;     // k-steps per fragment
+    constexpr int RP = RBN * 32;   // row capacity
     constexpr int QST = D + 8;     // LDS row stride in elements (16 bytes of padding)
-    __shared__ __attribute__((aligned(16))) uint16_t q_lds[RP * QST];
+    constexpr int CPK = D / 8;     // 16-byte chunks per key row
+    constexpr int KPI = 64 / CPK;  // keys per coalesced wave load
+    constexpr int NBUF = (RP > 128 ? RP : 128) * QST;
+    // q_lds holds the query rows during the passes and, before that, four
+    // per-wave staging areas of 32 key rows each (same row stride)
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[NBUF];
     __shared__ float2 red[4][RP];
     __shared__ __attribute__((aligned(16))) float lse_lds[RP];
-    __shared__ float2 wred[4];  // per-wave (max, sum) of an owned row
+    __shared__ float2 wred[4];  // per-wave (reference, sum) of an owned row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int col = lane & 15;
-    const int lg = lane >> 4;
+    const int col = lane & 31;
+    const int hf = lane >> 5;
     const int p = blockIdx.x / a.wg_per_stream;
     const int r = blockIdx.x - p * a.wg_per_stream;
     const int team = r / a.team_wgs;
@@ -175,9 +149,14 @@ kres_kernel(KresArgs a) {
     if (wi >= a.n_act) return;  // no keys for this work-group
     const int gt = p * a.n_teams + team;
     const int sstride = 2 * a.n_teams;
-    const int kbase = wi * (4 * KB * 16) + wave * (KB * 16);  // first key of this wave
-    const bool edge = kbase + KB * 16 > a.Np;  // reaches the window (causal mask) or the end
+    const int kbase = wi * (4 * KB * 32) + wave * (KB * 32);  // first key of this wave
+    const bool edge = kbase + KB * 32 > a.Np;  // reaches the window (causal mask) or the end
     uint32_t* abort_word = a.abort_word;
+    uint16_t* stage = q_lds + wave * 32 * QST;
+    uint32_t* tent = a.turn + cu_key() * 4u;
+    if (tid == 0) __hip_atomic_fetch_add(tent + p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool solo = false;
+    int nload = 0;  // slabs whose keys this work-group has loaded
 
     for (int s = gt; s < a.S; s += sstride) {
         const int g = s % a.Hkv;
@@ -186,47 +165,65 @@ kres_kernel(KresArgs a) {
         const uint16_t* kslab = a.k + l * a.ks[0] + b * a.ks[1] + g * a.ks[2];
         const uint16_t* qbase = a.q + l * a.qs[0] + b * a.qs[1];
 
-        __syncthreads();  // the previous slab is done with LDS
-        // --- this wave's keys, as operand fragments (clamped loads past the end);
-        //     issued first so they are in flight while the queries are staged
+        if (tid == 0) turn_wait(tent, p, nload, solo);
+        __syncthreads();  // the previous slab is done with LDS; this work-group's turn to load
+        // --- this wave's keys: coalesced loads (KPI whole rows per instruction,
+        //     clamped past the end), then reshaped through LDS into operand
+        //     fragments: fragment (kb, ks) of lane l holds elements
+        //     ks*16 + hf*8 .. +7 of key kbase + kb*32 + col
+        bf16x8 kst[KB][KS];
+        {
+            // key kbase + i*KPI + lane/CPK at step i (i = kb*KS + t): one pointer,
+            // advanced by a uniform stride and clamped to the last key
+            const uint16_t* kp = kslab + (int64_t)(kbase + lane / CPK) * a.ks[3] + (lane % CPK) * 8;
+            const uint16_t* klast = kslab + (int64_t)(a.N - 1) * a.ks[3] + (lane % CPK) * 8;
+            const int64_t kstep = (int64_t)KPI * a.ks[3];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int t = 0; t < KS; ++t) {
+                    kst[kb][t] = *reinterpret_cast<const bf16x8*>(kp < klast ? kp : klast);
+                    kp += kstep;
+                }
+        }
+        // --- the query rows of KV head g (row r -> head g*G + r/w, window index
+        //     r%w), loaded now and stored to LDS once the keys are reshaped
+        constexpr int QPER = (RP * CPK + 255) / 256;
+        uint4 qv[QPER];
+#pragma unroll
+        for (int u = 0; u < QPER; ++u) {
+            const int idx = tid + u * 256;
+            const int row = idx / CPK;
+            const int ch = idx - row * CPK;
+            qv[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < a.R) {
+                const int h = g * a.G + row / a.w;
+                const int i = row % a.w;
+                qv[u] = *reinterpret_cast<const uint4*>(qbase + h * a.qs[2] + i * a.qs[3] + ch * 8);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // every key and query load has landed: the partner may load
+        if (tid == 0) st32(tent + 2 + p, (uint32_t)(++nload));
         bf16x8 kf[KB][KS];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const int j = min(kbase + kb * 16 + col, a.N - 1);
-            const uint16_t* row = kslab + (int64_t)j * a.ks[3] + lg * 8;
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+                *reinterpret_cast<bf16x8*>(stage + (t * KPI + lane / CPK) * QST + (lane % CPK) * 8) = kst[kb][t];
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[kb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + ks * 32));
+                kf[kb][ks] = *reinterpret_cast<const bf16x8*>(stage + col * QST + ks * 16 + hf * 8);
+            __builtin_amdgcn_wave_barrier();
         }
-        // --- stage the query rows of KV head g (row r -> head g*G + r/w, window
-        //     index r%w) in LDS: every load is issued before the first store
-        {
-            constexpr int CH = D / 8;                // 16-byte chunks per row
-            constexpr int PER = (RP * CH + 255) / 256;
-            constexpr int BATCH = PER < 8 ? PER : 8;  // loads in flight per thread
+        __syncthreads();  // every wave has its fragments; the staging areas become q_lds
 #pragma unroll
-            for (int u0 = 0; u0 < PER; u0 += BATCH) {
-                uint4 qv[BATCH];
-#pragma unroll
-                for (int u = 0; u < BATCH; ++u) {
-                    const int idx = tid + (u0 + u) * 256;
-                    const int row = idx / CH;
-                    const int ch = idx - row * CH;
-                    qv[u] = make_uint4(0u, 0u, 0u, 0u);
-                    if (row < a.R) {
-                        const int h = g * a.G + row / a.w;
-                        const int i = row % a.w;
-                        qv[u] = *reinterpret_cast<const uint4*>(qbase + h * a.qs[2] + i * a.qs[3] + ch * 8);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < BATCH; ++u) {
-                    const int idx = tid + (u0 + u) * 256;
-                    const int row = idx / CH;
-                    const int ch = idx - row * CH;
-                    if (row < RP) *reinterpret_cast<uint4*>(q_lds + row * QST + ch * 8) = qv[u];
-                }
-            }
+        for (int u = 0; u < QPER; ++u) {
+            const int idx = tid + u * 256;
+            const int row = idx / CPK;
+            const int ch = idx - row * CPK;
+            if (row < RP) *reinterpret_cast<uint4*>(q_lds + row * QST + ch * 8) = qv[u];
         }
         __syncthreads();
 
@@ -236,20 +233,20 @@ kres_kernel(KresArgs a) {
             bf16x8 qf[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rb * 16 + col) * QST + ks * 32 + lg * 8);
-            // lane holds row rb*16 + col and keys kbase + kb*16 + 4*lg + v
+                qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rb * 32 + col) * QST + ks * 16 + hf * 8);
+            // lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
             float m, z;
             if (edge) {
-                const int row = rb * 16 + col;
+                const int row = rb * 32 + col;
                 const int lim = row < a.R ? a.Np + row % a.w : -1;
-                pass1_block<D, KB, true>(kf, qf, a.c, kbase + 4 * lg, lim, m, z);
+                z = pass1_max<D, KB, true>(kf, qf, a.c, kbase, hf, lim, m);
             } else {
-                pass1_block<D, KB, false>(kf, qf, a.c, kbase + 4 * lg, 0, m, z);
+                z = pass1_fast<D, KB>(kf, qf, a.c, m);
+                if (__any(!(z < kOverflow))) z = pass1_max<D, KB, false>(kf, qf, a.c, kbase, hf, 0, m);
             }
-            // merge the four lane groups (same row, other keys)
-#pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) merge(m, z, __shfl_xor(m, off), __shfl_xor(z, off));
-            if (lg == 0) red[wave][rb * 16 + col] = make_float2(m, z);
+            // merge the two lane halves (same row, other keys)
+            merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
+            if (hf == 0) red[wave][rb * 32 + col] = make_float2(m, z);
         }
         __syncthreads();
         uint64_t* part_s = a.part + (int64_t)s * a.team_wgs * RP;
@@ -304,44 +301,57 @@ kres_kernel(KresArgs a) {
         }
         ok = __syncthreads_and(ok) != 0;
 
-        // --- pass 2: per key, sum over all rows of exp2(x - LSE2)
+        // --- pass 2: per key, sum over all rows of exp2(x - LSE2); lane holds
+        //     key kbase + kb*32 + col and rows rb*32 + tile_row(v, hf)
         float cs[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) cs[kb] = 0.f;
 #pragma unroll 1
         for (int rb = 0; rb < a.rbn; ++rb) {
-            {
-                bf16x8 qf[KS];
+            bf16x8 qf[KS];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rb * 16 + col) * QST + ks * 32 + lg * 8);
-                const float4 lr = *reinterpret_cast<const float4*>(lse_lds + rb * 16 + 4 * lg);
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ks] = *reinterpret_cast<const bf16x8*>(q_lds + (rb * 32 + col) * QST + ks * 16 + hf * 8);
+            float lr[16];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < 4; ++u) {
+                const float4 t = *reinterpret_cast<const float4*>(lse_lds + rb * 32 + 8 * u + 4 * hf);
+                lr[4 * u] = t.x;
+                lr[4 * u + 1] = t.y;
+                lr[4 * u + 2] = t.z;
+                lr[4 * u + 3] = t.w;
+            }
+            f32x16 cur = logits<KS>(qf, kf[0]);
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) acc = mma(qf[ks], kf[kb][ks], acc);
-                    // lane holds key kbase + kb*16 + col and rows rb*16 + 4*lg + v
-                    cs[kb] += fexp2(acc[0] * a.c - lr.x) + fexp2(acc[1] * a.c - lr.y) +
-                              fexp2(acc[2] * a.c - lr.z) + fexp2(acc[3] * a.c - lr.w);
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x16 nxt;
+                if (kb + 1 < KB) nxt = logits<KS>(qf, kf[kb + 1]);
+                float t0s = 0.f, t1s = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    t0s += fexp2(cur[v] * a.c - lr[v]);
+                    t1s += fexp2(cur[v + 1] * a.c - lr[v + 1]);
                 }
+                cs[kb] += t0s + t1s;
+                if (kb + 1 < KB) cur = nxt;
             }
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            float v = cs[kb];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            const int j = kbase + kb * 16 + col;
-            if (lg == 0 && j < a.Np) a.raw[(int64_t)s * a.Np + j] = ok ? v * a.invG : NAN;
+            const float v = cs[kb] + __shfl_xor(cs[kb], 32);
+            const int j = kbase + kb * 32 + col;
+            if (hf == 0 && j < a.Np) a.raw[(int64_t)s * a.Np + j] = ok ? v * a.invG : NAN;
         }
     }
+    if (tid == 0) st32(tent + 2 + p, 0x7fffffffu);  // no more loads from this work-group
 }
 
 // Fill the exchange slots with the all-ones sentinel and clear the abort word.
-__global__ void kres_clear_kernel(uint64_t* slots, int64_t n64, uint32_t* abort_word) {
+__global__ void kres_clear_kernel(uint64_t* slots, int64_t n64, uint32_t* abort_word, uint32_t* turn) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n64; i += (int64_t)gridDim.x * blockDim.x)
         st64(slots + i, kEmpty64);
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < kTurnKeys * 4; i += gridDim.x * blockDim.x)
+        st32(turn + i, 0u);
     if (blockIdx.x == 0 && threadIdx.x == 0) st32(abort_word, 0u);
 }
 
@@ -354,7 +364,6 @@ kres_fn pick_rbn(int RBN) {
         case 2: return kres_kernel<D, KB, 2>;
         case 4: return kres_kernel<D, KB, 4>;
         case 8: return kres_kernel<D, KB, 8>;
-        case 16: return kres_kernel<D, KB, 16>;
         default: return nullptr;
     }
 }
@@ -365,7 +374,6 @@ kres_fn pick_kb(int KB, int RBN) {
         case 1: return pick_rbn<D, 1>(RBN);
         case 2: return pick_rbn<D, 2>(RBN);
         case 4: return pick_rbn<D, 4>(RBN);
-        case 8: return pick_rbn<D, 8>(RBN);
         default: return nullptr;
     }
 }
@@ -387,27 +395,28 @@ bool kres_plan(int dtype, int head_dim, int R, int64_t N, int64_t S, int n_cu, K
     plan.head_dim = head_dim;
     if (dtype != KVSEL_DTYPE_BF16 || (head_dim != 64 && head_dim != 128)) return false;
     if (R > 256 || n_cu < 1 || N < 1) return false;
-    constexpr int kKeysPerWgMax = 4 * 8 * 16;  // 4 waves x 8 key blocks x 16 keys
+    constexpr int kKeysPerWgMax = 4 * 4 * 32;  // 4 waves x 4 key blocks x 32 keys
     const int64_t team = (N + kKeysPerWgMax - 1) / kKeysPerWgMax;
     if (team > n_cu) return false;  // keys do not fit in one team's registers
     plan.team_wgs = (int)team;
     const int64_t per_wave = (N + team * 4 - 1) / (team * 4);
-    plan.kb = pow2_at_least((int)((per_wave + 15) / 16));
-    plan.n_act = (int)((N + plan.kb * 64 - 1) / (plan.kb * 64));
+    plan.kb = pow2_at_least((int)((per_wave + 31) / 32));
+    plan.n_act = (int)((N + plan.kb * 128 - 1) / (plan.kb * 128));
     int64_t teams = n_cu / plan.team_wgs;
     const int64_t need = (S + 1) / 2;  // teams per stream that have any slab
     if (teams > need) teams = need;
     if (teams < 1) teams = 1;
     plan.n_teams = (int)teams;
     plan.wg_per_stream = plan.n_teams * plan.team_wgs;
-    plan.rbn_cap = pow2_at_least((R + 15) / 16);
-    plan.rbn = (R + 15) / 16;
-    plan.rp = plan.rbn_cap * 16;
+    plan.rbn_cap = pow2_at_least((R + 31) / 32);
+    plan.rbn = (R + 31) / 32;
+    plan.rp = plan.rbn_cap * 32;
     plan.part_off = 0;
     plan.lse2_off = (size_t)S * plan.team_wgs * plan.rp * sizeof(uint64_t);
     plan.slots_end = plan.lse2_off + (((size_t)S * plan.rp * sizeof(float) + 7) & ~(size_t)7);
     plan.abort_off = align256(plan.slots_end);
-    plan.raw_off = align256(plan.abort_off + sizeof(uint32_t));
+    plan.turn_off = align256(plan.abort_off + sizeof(uint32_t));
+    plan.raw_off = align256(plan.turn_off + (size_t)kTurnKeys * 4 * sizeof(uint32_t));
     plan.total = plan.raw_off;  // + raw, added by the caller (shared with the general path)
     plan.ok = true;
     return true;
@@ -419,7 +428,8 @@ hipError_t launch_kres(const KresPlan& plan, KresArgs a, hipStream_t st) {
     int64_t blocks = (a.n_slots + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(kres_clear_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.slots, a.n_slots, a.abort_word);
+    hipLaunchKernelGGL(kres_clear_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.slots, a.n_slots, a.abort_word,
+                       a.turn);
     hipLaunchKernelGGL(fn, dim3(2 * plan.wg_per_stream), dim3(256), 0, st, a);
     return hipGetLastError();
 }

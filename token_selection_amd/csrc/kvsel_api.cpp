@@ -5,6 +5,8 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <hip/hip_runtime.h>
 
@@ -90,19 +92,40 @@ int device_cu_count() {
 struct Plan {
     ScoreGeom g;
     int RB;
-    ScoreWs gen;       // general two-pass layout
-    kvsel::KresPlan kres;  // register-resident layout (kres.ok when eligible)
-    size_t total;
+    ScoreWs gen;               // general two-pass layout (any dtype)
+    kvsel::StreamPlan stream;  // streaming bf16 layout (stream.ok when eligible)
+    kvsel::KresPlan kres;      // register-resident bf16 layout (kres.ok when eligible)
+    size_t stream_total, kres_total, total;
 };
+
+size_t raw_bytes(const ScoreGeom& g) { return ((size_t)g.S * g.Np * sizeof(float) + 255) & ~(size_t)255; }
 
 void make_plan(const kvsel_score_desc_t* d, Plan& p) {
     make_geom(d, p.g, p.RB);
     p.gen = ws_layout(p.g);
     p.total = p.gen.total;
-    if (kvsel::kres_plan(d->dtype, d->head_dim, p.g.R, p.g.N, p.g.S, device_cu_count(), p.kres)) {
-        p.kres.total = p.kres.raw_off + (((size_t)p.g.S * p.g.Np * sizeof(float) + 255) & ~(size_t)255);
-        if (p.kres.total > p.total) p.total = p.kres.total;
+    const int n_cu = device_cu_count();
+    p.stream_total = p.kres_total = 0;
+    if (kvsel::stream_plan(d->dtype, d->head_dim, p.g.R, p.g.N, p.g.Np, p.g.S, n_cu, p.stream)) {
+        p.stream_total = p.stream.raw_off + raw_bytes(p.g);
+        if (p.stream_total > p.total) p.total = p.stream_total;
     }
+    if (kvsel::kres_plan(d->dtype, d->head_dim, p.g.R, p.g.N, p.g.S, n_cu, p.kres)) {
+        p.kres_total = p.kres.raw_off + raw_bytes(p.g);
+        if (p.kres_total > p.total) p.total = p.kres_total;
+    }
+}
+
+// Scoring path: KVSEL_SCORE_PATH = "stream", "resident" or "general" forces
+// one where it applies; by default the streaming path for bf16, else general.
+enum class Path { Stream, Resident, General };
+
+Path choose_path(const Plan& p) {
+    const char* env = getenv("KVSEL_SCORE_PATH");
+    if (env && strcmp(env, "resident") == 0 && p.kres.ok && kvsel::kres_fits(p.kres)) return Path::Resident;
+    if (env && strcmp(env, "general") == 0) return Path::General;
+    if (p.stream.ok) return Path::Stream;
+    return Path::General;
 }
 
 kvsel_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
@@ -149,7 +172,35 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
     g.lse_out = lse_out;
     float* raw = nullptr;
     bool done = false;
-    if (p.kres.ok && kvsel::kres_fits(p.kres)) {
+    const Path path = choose_path(p);
+    if (path == Path::Stream) {
+        kvsel::StreamArgs a;
+        a.q = static_cast<const uint16_t*>(q_win);
+        a.k = static_cast<const uint16_t*>(k);
+        for (int i = 0; i < 4; ++i) {
+            a.qs[i] = g.qs[i];
+            a.ks[i] = g.ks[i];
+        }
+        a.B = g.B;
+        a.Hq = g.Hq;
+        a.Hkv = g.Hkv;
+        a.G = g.G;
+        a.w = g.w;
+        a.R = g.R;
+        a.rbn = p.stream.rbn;
+        a.N = (int32_t)g.N;
+        a.Np = (int32_t)g.Np;
+        a.S = g.S;
+        a.c = g.c;
+        a.invG = g.invG;
+        a.part = reinterpret_cast<float2*>(ws + p.stream.part_off);
+        a.lse2 = reinterpret_cast<float*>(ws + p.stream.lse2_off);
+        a.raw = reinterpret_cast<float*>(ws + p.stream.raw_off);
+        if (kvsel::launch_stream(p.stream, a, lse_out, hs) != hipSuccess) return KVSEL_ERR_HIP;
+        raw = a.raw;
+        done = true;
+    }
+    if (path == Path::Resident) {
         kvsel::KresArgs a;
         a.q = static_cast<const uint16_t*>(q_win);
         a.k = static_cast<const uint16_t*>(k);
@@ -178,6 +229,7 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
         a.slots = reinterpret_cast<uint64_t*>(ws + p.kres.part_off);
         a.n_slots = (int64_t)((p.kres.slots_end - p.kres.part_off) / sizeof(uint64_t));
         a.abort_word = reinterpret_cast<uint32_t*>(ws + p.kres.abort_off);
+        a.turn = reinterpret_cast<uint32_t*>(ws + p.kres.turn_off);
         a.raw = reinterpret_cast<float*>(ws + p.kres.raw_off);
         a.lse_out = lse_out;
         a.spin_limit = 100000000;  // 1 s of the 100 MHz wall clock

@@ -64,6 +64,7 @@ struct KresArgs {
     uint64_t* slots;  // part and lse2 as one span of n_slots 64-bit words (sentinel-filled)
     int64_t n_slots;
     uint32_t* abort_word;
+    uint32_t* turn;   // per-CU load-turn table (zero-filled before the launch)
     float* raw;       // [S][Np]
     float* lse_out;   // [L][B][Hq][w] or null
     int64_t spin_limit;  // wall-clock ticks (100 MHz) a wait may last
@@ -73,12 +74,40 @@ struct KresPlan {
     bool ok;
     int head_dim;
     int kb, team_wgs, n_teams, n_act, wg_per_stream, rbn, rbn_cap, rp;
-    size_t part_off, lse2_off, slots_end, abort_off, raw_off, total;
+    size_t part_off, lse2_off, slots_end, abort_off, turn_off, raw_off, total;
 };
 
 bool kres_plan(int dtype, int head_dim, int R, int64_t N, int64_t S, int n_cu, KresPlan& plan);
 bool kres_fits(const KresPlan& plan);
 hipError_t launch_kres(const KresPlan& plan, KresArgs a, hipStream_t stream);
+
+// Streaming path (bf16): pass 1 partials, merge, pass 2, each streaming K.
+struct StreamArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    int64_t qs[4];
+    int64_t ks[4];
+    int32_t B, Hq, Hkv, G, w, R, rbn;
+    int32_t N, Np, S;
+    int32_t spp;      // segments per slab (set per pass)
+    int32_t seg_len;  // keys per segment, a multiple of the 256-key chunk
+    int32_t n_range;  // keys the pass covers: N (pass 1) or Np (pass 2)
+    int32_t n_seg;    // S * spp
+    float c, invG;
+    float2* part;  // [S][spp1][rp] per-segment (reference, sum) of every row, log2 domain
+    float* lse2;   // [S][rp] row LSE2
+    float* raw;    // [S][Np]
+};
+
+struct StreamPlan {
+    bool ok;
+    int head_dim, rbn, rbn_cap, rp, n_wg;
+    int spp1, seg_len1, spp2, seg_len2;
+    size_t part_off, lse2_off, raw_off;  // raw: [S][Np] floats at raw_off
+};
+
+bool stream_plan(int dtype, int head_dim, int R, int64_t N, int64_t Np, int64_t S, int n_cu, StreamPlan& plan);
+hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, hipStream_t stream);
 
 hipError_t launch_accumulate(int32_t B, int32_t H, int64_t n, const float* src, float* dst, int mode,
                              hipStream_t stream);

@@ -1,0 +1,397 @@
+// Streaming two-pass saliency kernels (bf16, head_dim 64 or 128).
+//
+// The score of a prefix key needs the final log-sum-exp of every window row,
+// which depends on every key of the (layer, sequence, KV head) slab. These
+// kernels take the two passes literally and stream K from HBM in each:
+//
+//   stream_kernel<PASS=1>  per-row (reference, sum of exp2) partials of every
+//                          segment of a slab, causal mask applied;
+//   stream_merge_kernel    the partials of a slab's segments -> row LSE2 (and
+//                          the natural-log LSE the caller may ask for);
+//   stream_kernel<PASS=2>  per prefix key, sum over the rows of
+//                          exp2(c*x - LSE2), times 1/G -> raw scores.
+//
+// No work-group waits for another: every slab is cut into segments of whole
+// 256-key chunks, work-group g takes segments g, g + grid, ..., and while it
+// computes one chunk the loads of its next chunk are in flight into a second
+// register buffer, so HBM sees a continuous stream of requests. Each wave
+// holds 64 keys of a chunk as 32x32x16 operand fragments (tile32.h) and
+// reads its query fragments from the slab's rows staged in LDS.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "kvsel.h"
+#include "kvsel_internal.h"
+#include "tile32.h"
+
+namespace kvsel {
+namespace {
+
+using namespace tile;
+
+constexpr int kWaves = 4;
+constexpr int kKB = 2;                     // 32-key blocks per wave and chunk
+constexpr int kWaveKeys = kKB * 32;        // 64
+constexpr int kChunk = kWaves * kWaveKeys; // 256 keys per work-group chunk
+
+template <int D>
+struct Frag {
+    bf16x8 v[kKB][D / 16];
+};
+
+// Position in a work-group's sequence of chunks.
+struct Cursor {
+    int seg;    // segment index (slab * spp + part)
+    int first;  // first key of the chunk
+    int end;    // end of the segment's key range
+};
+
+__device__ __forceinline__ bool seg_range(const StreamArgs& a, int seg, int& first, int& end) {
+    const int part = seg % a.spp;
+    first = part * a.seg_len;
+    end = min(first + a.seg_len, a.n_range);
+    return first < end;
+}
+
+// The chunk after c in this work-group's sequence; seg = -1 when there is none.
+__device__ __forceinline__ Cursor advance(const StreamArgs& a, Cursor c) {
+    if (c.first + kChunk < c.end) return Cursor{c.seg, c.first + kChunk, c.end};
+    for (int seg = c.seg + (int)gridDim.x; seg < a.n_seg; seg += gridDim.x) {
+        int first, end;
+        if (seg_range(a, seg, first, end)) return Cursor{seg, first, end};
+    }
+    return Cursor{-1, 0, 0};
+}
+
+__device__ __forceinline__ const uint16_t* slab_keys(const StreamArgs& a, int slab) {
+    const int g = slab % a.Hkv;
+    const int b = (slab / a.Hkv) % a.B;
+    const int l = slab / (a.Hkv * a.B);
+    return a.k + l * a.ks[0] + b * a.ks[1] + g * a.ks[2];
+}
+
+// This wave's 64 keys of a chunk as operand fragments: lane (col, hf) reads
+// elements ks*16 + hf*8 .. +7 of key kbase + kb*32 + col (clamped to the last key).
+template <int D>
+__device__ __forceinline__ void load_chunk(Frag<D>& f, const StreamArgs& a, const Cursor& c, int wave, int col,
+                                           int hf) {
+    const uint16_t* kslab = slab_keys(a, c.seg / a.spp);
+    const int kbase = c.first + wave * kWaveKeys;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+        const int j = min(kbase + kb * 32 + col, a.N - 1);
+        const uint16_t* row = kslab + (int64_t)j * a.ks[3] + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            f.v[kb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + ks * 16));
+    }
+}
+
+template <int D, int RBN>
+struct Smem {
+    static constexpr int RP = RBN * 32;
+    static constexpr int QST = D + 8;  // LDS row stride in elements (16 bytes of padding)
+    uint16_t q[RP * QST];
+    float2 st[kWaves][RP];  // pass 1: running (reference, sum) per wave and row
+    float lse[RP];          // pass 2: row LSE2 (+inf on padded rows)
+};
+
+// Stage the query rows of a segment's slab (row r -> head g*G + r/w, window
+// index r%w; rows past R are zero) and reset or load the per-row state.
+template <int D, int RBN, int PASS>
+__device__ void stage(Smem<D, RBN>& sm, const StreamArgs& a, int seg, int tid) {
+    constexpr int RP = RBN * 32;
+    constexpr int QST = D + 8;
+    constexpr int CPK = D / 8;  // 16-byte chunks per row
+    constexpr int QPER = (RP * CPK + 255) / 256;
+    const int slab = seg / a.spp;
+    const int g = slab % a.Hkv;
+    const int b = (slab / a.Hkv) % a.B;
+    const int l = slab / (a.Hkv * a.B);
+    const uint16_t* qbase = a.q + l * a.qs[0] + b * a.qs[1];
+    __syncthreads();  // every wave is done with the previous segment's rows
+    uint4 qv[QPER];
+#pragma unroll
+    for (int u = 0; u < QPER; ++u) {
+        const int idx = tid + u * 256;
+        const int row = idx / CPK;
+        const int ch = idx - row * CPK;
+        qv[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (row < a.R) {
+            const int h = g * a.G + row / a.w;
+            const int i = row % a.w;
+            qv[u] = *reinterpret_cast<const uint4*>(qbase + h * a.qs[2] + i * a.qs[3] + ch * 8);
+        }
+    }
+    if (PASS == 1) {
+        for (int i = tid; i < kWaves * RP; i += 256) (&sm.st[0][0])[i] = make_float2(kNegBig, 0.f);
+    } else {
+        for (int row = tid; row < RP; row += 256) sm.lse[row] = row < a.R ? a.lse2[(int64_t)slab * RP + row] : INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < QPER; ++u) {
+        const int idx = tid + u * 256;
+        const int row = idx / CPK;
+        const int ch = idx - row * CPK;
+        if (row < RP) *reinterpret_cast<uint4*>(sm.q + row * QST + ch * 8) = qv[u];
+    }
+    __syncthreads();
+}
+
+// Pass 1 on one chunk: merge this wave's (reference, sum) of every row into
+// its running state.
+template <int D, int RBN>
+__device__ __forceinline__ void pass1_chunk(Smem<D, RBN>& sm, const StreamArgs& a, const Frag<D>& f,
+                                            const Cursor& c, int wave, int col, int hf) {
+    constexpr int KS = D / 16;
+    constexpr int QST = D + 8;
+    const int kbase = c.first + wave * kWaveKeys;
+    if (kbase >= a.N) return;  // the chunk ends before this wave's keys
+    const bool edge = kbase + kWaveKeys > a.Np;  // reaches the window (causal mask) or the end
+#pragma unroll 1
+    for (int rb = 0; rb < a.rbn; ++rb) {
+        bf16x8 qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(sm.q + (rb * 32 + col) * QST + ks * 16 + hf * 8);
+        // lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
+        float m, z;
+        if (edge) {
+            const int row = rb * 32 + col;
+            const int lim = row < a.R ? a.Np + row % a.w : -1;
+            z = pass1_max<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m);
+        } else {
+            z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
+            if (__any(!(z < kOverflow))) z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
+        }
+        merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));  // the two lane halves: same row, other keys
+        if (hf == 0) {
+            float2 st = sm.st[wave][rb * 32 + col];
+            merge(st.x, st.y, m, z);
+            sm.st[wave][rb * 32 + col] = st;
+        }
+    }
+}
+
+// Pass 2 on one chunk: raw score of each of this wave's prefix keys.
+template <int D, int RBN>
+__device__ __forceinline__ void pass2_chunk(Smem<D, RBN>& sm, const StreamArgs& a, const Frag<D>& f,
+                                            const Cursor& c, int wave, int col, int hf) {
+    constexpr int KS = D / 16;
+    constexpr int QST = D + 8;
+    const int kbase = c.first + wave * kWaveKeys;
+    if (kbase >= a.Np) return;  // no prefix keys in this wave's range
+    float cs0 = 0.f, cs1 = 0.f;
+#pragma unroll 1
+    for (int rb = 0; rb < a.rbn; ++rb) {
+        bf16x8 qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(sm.q + (rb * 32 + col) * QST + ks * 16 + hf * 8);
+        float lr[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float4 t = *reinterpret_cast<const float4*>(sm.lse + rb * 32 + 8 * u + 4 * hf);
+            lr[4 * u] = t.x;
+            lr[4 * u + 1] = t.y;
+            lr[4 * u + 2] = t.z;
+            lr[4 * u + 3] = t.w;
+        }
+        // lane holds key kbase + kb*32 + col and rows rb*32 + tile_row(v, hf)
+        const f32x16 x0 = logits<KS>(qf, f.v[0]);
+        const f32x16 x1 = logits<KS>(qf, f.v[1]);  // in the matrix core while x0 is exponentiated
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+            s0 += fexp2(x0[v] * a.c - lr[v]);
+            s1 += fexp2(x0[v + 1] * a.c - lr[v + 1]);
+        }
+        cs0 += s0 + s1;
+        s0 = 0.f;
+        s1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+            s0 += fexp2(x1[v] * a.c - lr[v]);
+            s1 += fexp2(x1[v + 1] * a.c - lr[v + 1]);
+        }
+        cs1 += s0 + s1;
+    }
+    const int slab = c.seg / a.spp;
+    const float v0 = cs0 + __shfl_xor(cs0, 32);
+    const float v1 = cs1 + __shfl_xor(cs1, 32);
+    const int j0 = kbase + col;
+    const int j1 = kbase + 32 + col;
+    if (hf == 0 && j0 < a.Np) a.raw[(int64_t)slab * a.Np + j0] = v0 * a.invG;
+    if (hf == 0 && j1 < a.Np) a.raw[(int64_t)slab * a.Np + j1] = v1 * a.invG;
+}
+
+// Pass 1, end of a segment: merge the waves' states and publish the partials.
+template <int D, int RBN>
+__device__ __forceinline__ void pass1_finish(Smem<D, RBN>& sm, const StreamArgs& a, int seg, int tid) {
+    constexpr int RP = RBN * 32;
+    __syncthreads();
+    for (int row = tid; row < RP; row += 256) {
+        float2 acc = sm.st[0][row];
+#pragma unroll
+        for (int w2 = 1; w2 < kWaves; ++w2) merge(acc.x, acc.y, sm.st[w2][row].x, sm.st[w2][row].y);
+        a.part[(int64_t)seg * RP + row] = acc;
+    }
+}
+
+// One chunk with its keys in `f` while the next chunk's keys load into `g`.
+// Returns false once the work-group's sequence ends.
+template <int D, int RBN, int PASS>
+__device__ __forceinline__ bool step(Smem<D, RBN>& sm, const StreamArgs& a, Cursor& cur, Frag<D>& f, Frag<D>& g,
+                                     int tid, int wave, int col, int hf) {
+    const Cursor nx = advance(a, cur);
+    if (nx.seg >= 0) load_chunk<D>(g, a, nx, wave, col, hf);
+    if (PASS == 1)
+        pass1_chunk<D, RBN>(sm, a, f, cur, wave, col, hf);
+    else
+        pass2_chunk<D, RBN>(sm, a, f, cur, wave, col, hf);
+    if (nx.seg != cur.seg) {
+        if (PASS == 1) pass1_finish<D, RBN>(sm, a, cur.seg, tid);
+        if (nx.seg < 0) return false;
+        stage<D, RBN, PASS>(sm, a, nx.seg, tid);
+    }
+    cur = nx;
+    return true;
+}
+
+template <int D, int RBN, int PASS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+stream_kernel(StreamArgs a) {
+    __shared__ __attribute__((aligned(16))) Smem<D, RBN> sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int hf = lane >> 5;
+
+    Cursor cur{-1, 0, 0};
+    for (int seg = blockIdx.x; seg < a.n_seg; seg += gridDim.x) {
+        int first, end;
+        if (seg_range(a, seg, first, end)) {
+            cur = Cursor{seg, first, end};
+            break;
+        }
+    }
+    if (cur.seg < 0) return;
+    Frag<D> fa, fb;
+    load_chunk<D>(fa, a, cur, wave, col, hf);
+    stage<D, RBN, PASS>(sm, a, cur.seg, tid);
+
+    for (;;) {
+        if (!step<D, RBN, PASS>(sm, a, cur, fa, fb, tid, wave, col, hf)) break;
+        if (!step<D, RBN, PASS>(sm, a, cur, fb, fa, tid, wave, col, hf)) break;
+    }
+}
+
+// Row LSE2 of every slab from its segments' partials; padded rows are left
+// alone (pass 2 stages +inf for them).
+__global__ void stream_merge_kernel(const float2* part, int spp, int rp, int R, int w, int B, int Hq, int Hkv,
+                                    int G, float* lse2, float* lse_out) {
+    const int slab = blockIdx.x;
+    for (int row = threadIdx.x; row < R; row += blockDim.x) {
+        float M = kNegBig, Z = 0.f;
+        for (int p = 0; p < spp; ++p) {
+            const float2 v = part[((int64_t)slab * spp + p) * rp + row];
+            merge(M, Z, v.x, v.y);
+        }
+        const float l2 = M + log2f(Z);
+        lse2[(int64_t)slab * rp + row] = l2;
+        if (lse_out) {
+            const int g = slab % Hkv;
+            const int b = (slab / Hkv) % B;
+            const int l = slab / (Hkv * B);
+            const int h = g * G + row / w;
+            const int i = row % w;
+            lse_out[(((int64_t)l * B + b) * Hq + h) * w + i] = l2 * 0.69314718055994530942f;
+        }
+    }
+}
+
+typedef void (*stream_fn)(StreamArgs);
+
+template <int D, int PASS>
+stream_fn pick_rbn(int RBN) {
+    switch (RBN) {
+        case 1: return stream_kernel<D, 1, PASS>;
+        case 2: return stream_kernel<D, 2, PASS>;
+        case 4: return stream_kernel<D, 4, PASS>;
+        case 8: return stream_kernel<D, 8, PASS>;
+        default: return nullptr;
+    }
+}
+
+stream_fn pick(int D, int RBN, int PASS) {
+    if (D == 128) return PASS == 1 ? pick_rbn<128, 1>(RBN) : pick_rbn<128, 2>(RBN);
+    return PASS == 1 ? pick_rbn<64, 1>(RBN) : pick_rbn<64, 2>(RBN);
+}
+
+int pow2_at_least(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Segments per slab for `keys` keys: about two per work-group slot of the
+// grid in total, each a whole number of chunks.
+void segments(int64_t keys, int64_t S, int n_wg, int& spp, int& seg_len) {
+    int64_t want = (2 * (int64_t)n_wg + S - 1) / S;
+    const int64_t chunks = (keys + kChunk - 1) / kChunk;
+    if (want > chunks) want = chunks;
+    if (want < 1) want = 1;
+    const int64_t per = (chunks + want - 1) / want;  // chunks per segment
+    seg_len = (int)(per * kChunk);
+    spp = (int)((keys + seg_len - 1) / seg_len);
+    if (spp < 1) spp = 1;
+}
+
+}  // namespace
+
+bool stream_plan(int dtype, int head_dim, int R, int64_t N, int64_t Np, int64_t S, int n_cu, StreamPlan& plan) {
+    plan.ok = false;
+    if (dtype != KVSEL_DTYPE_BF16 || (head_dim != 64 && head_dim != 128)) return false;
+    if (R < 1 || R > 256 || N < 1 || S < 1 || n_cu < 1) return false;
+    plan.head_dim = head_dim;
+    plan.rbn = (R + 31) / 32;
+    plan.rbn_cap = pow2_at_least(plan.rbn);
+    plan.rp = plan.rbn_cap * 32;
+    plan.n_wg = 2 * n_cu;
+    segments(N, S, plan.n_wg, plan.spp1, plan.seg_len1);
+    segments(Np > 0 ? Np : 1, S, plan.n_wg, plan.spp2, plan.seg_len2);
+    plan.part_off = 0;
+    plan.lse2_off = align256((size_t)S * plan.spp1 * plan.rp * sizeof(float2));
+    plan.raw_off = align256(plan.lse2_off + (size_t)S * plan.rp * sizeof(float));
+    plan.ok = pick(head_dim, plan.rbn_cap, 1) != nullptr;
+    return plan.ok;
+}
+
+hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, hipStream_t st) {
+    stream_fn f1 = pick(plan.head_dim, plan.rbn_cap, 1);
+    stream_fn f2 = pick(plan.head_dim, plan.rbn_cap, 2);
+    if (!f1 || !f2) return hipErrorInvalidValue;
+    // pass 1 over every key (window included)
+    a.spp = plan.spp1;
+    a.seg_len = plan.seg_len1;
+    a.n_range = a.N;
+    a.n_seg = a.S * plan.spp1;
+    hipLaunchKernelGGL(f1, dim3((unsigned)(a.n_seg < plan.n_wg ? a.n_seg : plan.n_wg)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.part, plan.spp1, plan.rp, a.R,
+                       a.w, a.B, a.Hq, a.Hkv, a.G, a.lse2, lse_out);
+    // pass 2 over the prefix keys
+    if (a.Np > 0) {
+        a.spp = plan.spp2;
+        a.seg_len = plan.seg_len2;
+        a.n_range = a.Np;
+        a.n_seg = a.S * plan.spp2;
+        hipLaunchKernelGGL(f2, dim3((unsigned)(a.n_seg < plan.n_wg ? a.n_seg : plan.n_wg)), dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvsel
