@@ -97,6 +97,11 @@ size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc);
  *         window row.
  * workspace  device, >= kvsel_score_workspace_bytes(desc) bytes, 256-byte
  *         aligned; its content is scratch between calls.
+ * Paths: bf16 with head_dim 64/128 and G*w <= 256 streams K in two passes;
+ * other shapes take a general two-pass path. The environment variable
+ * KVSEL_SCORE_PATH=resident (register-resident, single K read) or =general
+ * forces another path where it applies; every path computes the same result
+ * to the stated tolerance.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,

@@ -245,7 +245,9 @@ template <int D, int RBN, int PASS>
 __device__ __forceinline__ bool step(Smem<D, RBN>& sm, const StreamArgs& a, Cursor& cur, Frag<D>& f, Frag<D>& g,
                                      int tid, int wave, int col, int hf) {
     const Cursor nx = advance(a, cur);
-    if (nx.seg >= 0) load_chunk<D>(g, a, nx, wave, col, hf);
+    // Issued on every step (the last one re-reads the current chunk): with a
+    // fixed number of loads in flight the wait for `f` leaves `g`'s in flight.
+    load_chunk<D>(g, a, nx.seg >= 0 ? nx : cur, wave, col, hf);
     if (PASS == 1)
         pass1_chunk<D, RBN>(sm, a, f, cur, wave, col, hf);
     else
