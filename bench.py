@@ -97,6 +97,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="structkv_128k_16l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lse-in", action="store_true",
+                    help="score with the window rows' LSE handed in (kvsel_score_lse, one pass over K); the LSE "
+                         "is computed once before timing, as prefill attention would have it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -146,11 +149,20 @@ def main() -> int:
     def mk():
         return torch.cuda.Event(enable_timing=True)
 
+    lse_in = None
+    if args.lse_in:
+        lse_in = torch.empty(tuple(q.shape[:4]), dtype=torch.float32, device=dev)
+        K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc, lse_out=lse_in)
+        torch.cuda.synchronize()
+
     def step(evs=None):
         # evs: per-stage (start, end) events recorded on the launch stream
         if evs:
             evs["score"][0].record(stream)
-        K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
+        if lse_in is None:
+            K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
+        else:
+            K.kvsel_score_lse(q, k, lse_in, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
         if evs:
             evs["score"][1].record(stream)
             evs["topk"][0].record(stream)
@@ -208,17 +220,22 @@ def main() -> int:
         "data": "synthetic (seeded; no dataset or weights)",
         "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "n_keys": wl.n_keys, "window": wl.window,
-                   "pool": wl.pool_kernel, "kv_budget": wl.kv_budget},
+                   "pool": wl.pool_kernel, "kv_budget": wl.kv_budget,
+                   "lse": "computed (two passes)" if lse_in is None else "handed in (one pass)"},
         "hbm_gbs_whole_path": whole_gbs,
         "hbm_frac_whole_path": whole_gbs / HBM_PEAK_GBS,
         "stage_ms": stage_ms,
         # dominant launch group: the scoring call (kvsel_score: stream_kernel
         # pass 1, the LSE merge, stream_kernel pass 2 and the pool, 89% of the
-        # step's kernel time), timed with HIP events on its launch stream;
+        # step's kernel time; with --lse-in kvsel_score_lse: the LSE copy,
+        # pass 2 and the pool), timed with HIP events on its launch stream;
         # algorithmic bytes = K read once + Q + final scores
-        "roofline": {"bound": "hbm", "kernel": "kvsel_score (stream_kernel pass 1 + merge + pass 2 + pool)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("kvsel_score (stream_kernel pass 1 + merge + pass 2 + pool)" if lse_in is None
+                                else "kvsel_score_lse (stream_kernel pass 2 + pool)"),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic("kvsel_score", SCORE_SOURCES),
+                     "traffic": recorded_traffic("kvsel_score" if lse_in is None else "kvsel_score_lse",
+                                                 SCORE_SOURCES),
                      "algorithmic_bytes": score_alg_bytes},
         "cpu_baseline": cpu,
         "wall_s_timed": wall,

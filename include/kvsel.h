@@ -109,6 +109,23 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
                            void* stream);
 
 /*
+ * Saliency scores with the window rows' LSEs handed in: prefill attention
+ * (FastKV section 2A; StructKV section 1) has already normalised every window
+ * row, so only the second softmax pass runs and K is read once.
+ *
+ * Same arguments as kvsel_score, except:
+ * lse_in  device float[L][B][Hq][w], required: the natural-log LSE of every
+ *         window row under the same scale and causal mask (the layout
+ *         kvsel_score writes to lse_out). Values must be finite.
+ * workspace  >= kvsel_score_workspace_bytes(desc) bytes, 256-byte aligned.
+ * Scores equal kvsel_score's to the stated tolerance when lse_in is the LSE
+ * kvsel_score would compute. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+kvsel_status_t kvsel_score_lse(const kvsel_score_desc_t* desc, const void* q_win, const void* k, const float* lse_in,
+                               float* scores, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Accumulate score vectors (StructKV section 1: a token's scores added up over
  * layers; FastKV section 2A: one token set per sequence for propagation).
  *

@@ -7,6 +7,8 @@ from .kvsel_oracle import (
     row_lse,
     saliency_one,
     saliency_all,
+    saliency_given_lse,
+    saliency_all_given_lse,
     avg_pool,
     pooled_scores,
     accumulate_layers,
@@ -24,6 +26,8 @@ __all__ = [
     "row_lse",
     "saliency_one",
     "saliency_all",
+    "saliency_given_lse",
+    "saliency_all_given_lse",
     "avg_pool",
     "pooled_scores",
     "accumulate_layers",

@@ -171,6 +171,50 @@ def saliency_all(q: np.ndarray, k: np.ndarray, dtype: str, scale: Optional[float
     return lse, raw
 
 
+def saliency_given_lse(q: np.ndarray, k: np.ndarray, lse: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """One (layer, sequence) with the window rows' natural-log LSE handed in:
+    prefill attention has already normalised every window row (FastKV section
+    2A, StructKV section 1), so each key's score needs only its logits and the
+    given LSE: raw[g, j] = (1/G) sum over the G heads h of group g and the w
+    rows i of exp(l[h, i, j] - lse[h, i]), over the keys row i sees.
+
+    q: [Hq, w, d], k: [Hkv, N, d], lse: [Hq, w] float64 -> raw [Hkv, N].
+    """
+    Hq, w, d = q.shape
+    Hkv, N, _ = k.shape
+    G = Hq // Hkv
+    scale = default_scale(d) if scale is None else scale
+    raw = np.zeros((Hkv, N))
+    for h in range(Hq):
+        logits = window_logits(q[h], k[h // G], scale)
+        raw[h // G] += np.exp(logits - lse[h][:, None]).sum(axis=0)
+    return raw / G
+
+
+def saliency_all_given_lse(q: np.ndarray, k: np.ndarray, lse: np.ndarray, dtype: str,
+                           scale: Optional[float] = None, threads: int = 1) -> np.ndarray:
+    """saliency_given_lse over every (layer, sequence): q [L, B, Hq, w, d],
+    k [L, B, Hkv, N, d] (stored element type), lse [L, B, Hq, w] -> raw
+    [L, B, Hkv, N] float64."""
+    L, B = q.shape[:2]
+    raw = np.full((L, B, k.shape[2], k.shape[3]), np.nan)
+
+    def unit(args):
+        l, b = args
+        raw[l, b] = saliency_given_lse(to_f64(q[l, b], dtype), to_f64(k[l, b], dtype),
+                                       np.asarray(lse[l, b], dtype=np.float64), scale)
+
+    jobs = [(l, b) for l in range(L) for b in range(B)]
+    if threads <= 1:
+        for j in jobs:
+            unit(j)
+    else:
+        ctx = threadpool_limits(1) if threadpool_limits is not None else _null()
+        with ctx, cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(unit, jobs))
+    return raw
+
+
 class _null:
     def __enter__(self):
         return self
@@ -272,18 +316,25 @@ def gather_rows(src: np.ndarray, idx: np.ndarray) -> np.ndarray:
 def pipeline(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], *, dtype: str, window: int,
              pool_kernel: int, kv_budget: int, tsp_budget: Optional[int] = None,
              hidden: Optional[np.ndarray] = None, scale: Optional[float] = None,
-             threads: int = 1, heads: Optional[Sequence[int]] = None) -> dict:
+             threads: int = 1, heads: Optional[Sequence[int]] = None,
+             lse_in: Optional[np.ndarray] = None) -> dict:
     """Score every layer, accumulate over layers (StructKV; a single layer is
     its own sum), select per KV head with the KV budget, and gather K and V of
     every layer with those indices; with a TSP budget also rank the head-mean
-    score for one token set per sequence and gather the hidden rows.
+    score for one token set per sequence and gather the hidden rows. With
+    ``lse_in`` ([L, B, Hq, w] natural-log LSE of the window rows, handed in)
+    the scores use that LSE instead of computing it.
 
     Shapes: q [L, B, Hq, w, d]; k, v [L, B, Hkv, N, d]; hidden [B, N, D].
     """
     L, B, Hq, w, d = q.shape
     N = k.shape[3]
     Hkv = k.shape[2]
-    lse, raw = saliency_all(q, k, dtype, scale, threads=threads, heads=heads)
+    if lse_in is None:
+        lse, raw = saliency_all(q, k, dtype, scale, threads=threads, heads=heads)
+    else:
+        lse = np.asarray(lse_in, dtype=np.float64)
+        raw = saliency_all_given_lse(q, k, lse, dtype, scale, threads=threads)
     per_layer = pooled_scores(raw, window, pool_kernel)           # [L, B, Hkv, Np]
     scores = accumulate_layers(per_layer)                         # [B, Hkv, Np]
     hsel = list(range(Hkv)) if heads is None else list(heads)

@@ -39,6 +39,23 @@ def brute_saliency(q, k, scale):
     return lse, raw
 
 
+def brute_saliency_given_lse(q, k, lse, scale):
+    """As brute_saliency, with each window row's natural-log LSE given
+    (lse[Hq][w]) instead of computed: raw[g][j] = sum over the group's rows of
+    exp(logit - lse) / G."""
+    Hq, w, d = len(q), len(q[0]), len(q[0][0])
+    Hkv, N = len(k), len(k[0])
+    G = Hq // Hkv
+    raw = [[0.0] * N for _ in range(Hkv)]
+    for h in range(Hq):
+        g = h // G
+        for i in range(w):
+            for j in range(N - w + i + 1):
+                logit = scale * math.fsum(q[h][i][t] * k[g][j][t] for t in range(d))
+                raw[g][j] += math.exp(logit - lse[h][i]) / G
+    return raw
+
+
 def brute_pool(x, kernel):
     """Average pool, zero padded, divisor always ``kernel``."""
     r = (kernel - 1) // 2

@@ -52,25 +52,32 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None):
+def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None, lse_in=None):
     """The path as the benchmark runs it: one kvsel_score call over every
     layer, the per-KV-head select, the K/V gather over every layer, and (with
-    a TSP budget) head mean, token-set select and hidden gather."""
+    a TSP budget) head mean, token-set select and hidden gather. With
+    ``lse_in`` ([L, B, Hq, w] natural-log LSE) the scoring call is
+    kvsel_score_lse instead."""
     q = to_dev(inp["q"], wl.dtype)
     k = to_dev(inp["k"], wl.dtype)
     L, B, Hq, w, d = inp["q"].shape
     out = {}
-    lse = torch.full((L, B, Hq, w), float("nan"), device=device()) if with_lse else None
+    lse = torch.full((L, B, Hq, w), float("nan"), device=device()) if with_lse and lse_in is None else None
     if accumulate_into is not None:
         scores = torch.from_numpy(accumulate_into.astype(np.float32)).to(device())
     else:
         scores = torch.full((B, wl.n_kv_heads, wl.n_keys - wl.window), float("nan"), device=device())
-    K.kvsel_score(q, k, scores, window=wl.window, pool_kernel=wl.pool_kernel,
-                  accumulate=accumulate_into is not None, lse_out=lse)
+    if lse_in is None:
+        K.kvsel_score(q, k, scores, window=wl.window, pool_kernel=wl.pool_kernel,
+                      accumulate=accumulate_into is not None, lse_out=lse)
+    else:
+        lse_dev = torch.from_numpy(np.ascontiguousarray(lse_in, dtype=np.float32)).to(device())
+        K.kvsel_score_lse(q, k, lse_dev, scores, window=wl.window, pool_kernel=wl.pool_kernel,
+                          accumulate=accumulate_into is not None)
     idx = K.kvsel_topk(scores, n_keys=wl.n_keys, window=wl.window, budget=wl.kv_budget)
     out["scores"] = scores.cpu().numpy()
     out["idx"] = idx.cpu().numpy()
-    if with_lse:
+    if lse is not None:
         out["lse"] = lse.cpu().numpy()
     if with_gather and inp.get("v") is not None:
         v = to_dev(inp["v"], wl.dtype)
@@ -153,10 +160,10 @@ def assert_gather(kept: np.ndarray, src: np.ndarray, idx: np.ndarray, what: str)
                 raise AssertionError(f"{what}: gathered rows differ at layer {l}, batch {b}")
 
 
-def oracle_for(wl, inp, threads=8, heads=None):
+def oracle_for(wl, inp, threads=8, heads=None, lse_in=None):
     return oracle.pipeline(inp["q"], inp["k"], inp.get("v"), dtype=wl.dtype, window=wl.window,
                            pool_kernel=wl.pool_kernel, kv_budget=wl.kv_budget, tsp_budget=wl.tsp_budget,
-                           hidden=inp.get("hidden"), threads=threads, heads=heads)
+                           hidden=inp.get("hidden"), threads=threads, heads=heads, lse_in=lse_in)
 
 
 def check_all(wl, inp, gpu, ref, heads=None):

@@ -15,7 +15,7 @@ import math
 import numpy as np
 from scipy.special import logsumexp
 
-from brute_force import brute_pool, brute_saliency, brute_select
+from brute_force import brute_pool, brute_saliency, brute_saliency_given_lse, brute_select
 
 # tiny shapes: (Hq, Hkv, w, d, N, pool, budget)
 TINY_CASES = [
@@ -278,7 +278,43 @@ def check_widening(orc):
     assert list(out) == [1.0, -2.0, 0.333984375, 2.0 ** -133]
 
 
+def check_given_lse_brute(orc):
+    """Scores from a handed-in LSE == the separately written brute force, for
+    LSE values away from the true ones (random offsets per row)."""
+    rng = np.random.default_rng(77)
+    for (Hq, Hkv, w, d, N, pool, budget) in TINY_CASES:
+        q, k = _rand_case(rng, Hq, Hkv, w, d, N)
+        lse = rng.normal(2.0, 1.5, size=(Hq, w))
+        raw = orc.saliency_given_lse(q, k, lse)
+        braw = brute_saliency_given_lse(q.tolist(), k.tolist(), lse.tolist(), 1.0 / math.sqrt(d))
+        np.testing.assert_allclose(raw, np.array(braw), rtol=1e-11, atol=1e-15)
+
+
+def check_given_lse_mass_and_shift(orc):
+    """With the true LSE (scipy's logsumexp over the visible logits, computed
+    here) every row's probabilities sum to one, so each KV head's raw scores
+    sum to w; adding delta to every row's LSE scales every score by
+    exp(-delta)."""
+    rng = np.random.default_rng(78)
+    for (Hq, Hkv, w, d, N, pool, budget) in TINY_CASES:
+        q, k = _rand_case(rng, Hq, Hkv, w, d, N)
+        G = Hq // Hkv
+        scale = 1.0 / math.sqrt(d)
+        lse = np.empty((Hq, w))
+        for h in range(Hq):
+            for i in range(w):
+                vis = k[h // G, : N - w + i + 1] @ q[h, i] * scale
+                lse[h, i] = logsumexp(vis)
+        raw = orc.saliency_given_lse(q, k, lse)
+        np.testing.assert_allclose(raw.sum(axis=1), np.full(Hkv, float(w)), rtol=1e-12)
+        delta = 0.731
+        np.testing.assert_allclose(orc.saliency_given_lse(q, k, lse + delta), raw * math.exp(-delta),
+                                   rtol=1e-12, atol=1e-300)
+
+
 ALL_CHECKS = [
+    check_given_lse_brute,
+    check_given_lse_mass_and_shift,
     check_brute_force,
     check_pipeline_brute,
     check_zero_query_closed_form,

@@ -169,3 +169,15 @@ def test_topk_workspace_contract(lib):
     assert lib.kvsel_topk(1, 8, 131072, 32, 4096, FAKE, FAKE, None, need, None) == 3
     assert lib.kvsel_topk(1, 8, 131072, 32, 4096, FAKE, FAKE, FAKE, need - 1, None) == 3
     assert lib.kvsel_topk(1, 8, 131072, 32, 4096, FAKE, FAKE, FAKE + 16, need, None) == 3
+
+
+def test_score_lse_rejects(lib):
+    d = good_desc()
+    need = lib.kvsel_score_workspace_bytes(ctypes.byref(d))
+    # missing LSE, then the same descriptor and pointer checks as kvsel_score
+    assert lib.kvsel_score_lse(ctypes.byref(d), FAKE, FAKE, None, FAKE, 0, FAKE, need, None) == 1
+    assert lib.kvsel_score_lse(None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, need, None) == 1
+    assert lib.kvsel_score_lse(ctypes.byref(d), FAKE + 8, FAKE, FAKE, FAKE, 0, FAKE, need, None) == 1
+    assert lib.kvsel_score_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, need - 1, None) == 3
+    bad = good_desc(head_dim=96)
+    assert lib.kvsel_score_lse(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == 2

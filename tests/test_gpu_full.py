@@ -4,6 +4,8 @@ oracle on every score, LSE, kept index and gathered row."""
 
 import time
 
+import numpy as np
+
 import pytest
 
 from gpu_util import check_all, oracle_for, run_gpu, say
@@ -31,14 +33,19 @@ def inputs_and_oracle(name):
     return _CACHE[name]
 
 
-@pytest.mark.parametrize("path", ["stream", "resident"])
+@pytest.mark.parametrize("path", ["stream", "resident", "given_lse"])
 @pytest.mark.parametrize("name", ["llama8b_32k_tsp", "batched_8x32k_ar1", "qwen7b_512k", "structkv_128k_16l"])
 def test_full_workload(path, name, monkeypatch):
-    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
     wl, inp, ref = inputs_and_oracle(name)
     t0 = time.time()
     say(f"case {name} [{path}]: running the HIP path")
-    gpu = run_gpu(wl, inp)
+    if path == "given_lse":
+        # kvsel_score_lse with the oracle's exact LSE rounded to fp32: the
+        # oracle's scores are the reference (they were computed with that LSE)
+        gpu = run_gpu(wl, inp, lse_in=ref["lse"].astype(np.float32))
+    else:
+        monkeypatch.setenv("KVSEL_SCORE_PATH", path)
+        gpu = run_gpu(wl, inp)
     say(f"case {name} [{path}]: comparing ({time.time() - t0:.1f}s)")
     check_all(wl, inp, gpu, ref)
     say(f"case {name} [{path}]: done ({time.time() - t0:.1f}s)")

@@ -179,3 +179,43 @@ def test_strided_query_view():
     torch.cuda.synchronize()
     ref = oracle_for(wl, inp)
     assert_scores_close(s.cpu().numpy(), ref["scores"])
+
+
+LSE_CASES = [c for c in RAGGED if c[0] == "bf16" and c[3] // c[4] * c[7] <= 256] + [RAGGED[8], RAGGED[9]]
+
+
+@pytest.mark.parametrize("path", ["stream", "general"])
+@pytest.mark.parametrize("case", LSE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_scores_from_given_lse(case, path, monkeypatch):
+    """kvsel_score_lse (single pass, the window rows' LSE handed in) against the
+    oracle given the same LSE: the true LSE (fp32-rounded) and one shifted per
+    row by seeded offsets, so that the result is not the self-normalised one."""
+    dt, L, B, Hq, Hkv, d, N, w, pool, budget = case
+    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
+    say("case given-lse", case, path)
+    wl = TINY.with_(name="given_lse", wid=300 + LSE_CASES.index(case), dtype=dt, n_layers=L, batch=B,
+                    n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool,
+                    kv_budget=budget, n_hubs=min(8, max(0, N - w - 1)))
+    inp = make_inputs(wl)
+    ref0 = oracle_for(wl, inp)
+    offs = np.random.default_rng(99).normal(0.0, 0.7, size=ref0["lse"].shape)
+    for lse in (ref0["lse"], ref0["lse"] + offs):
+        lse32 = lse.astype(np.float32)
+        ref = oracle_for(wl, inp, lse_in=lse32.astype(np.float64))
+        gpu = run_gpu(wl, inp, lse_in=lse32)
+        check_all(wl, inp, gpu, ref)
+
+
+def test_given_lse_matches_two_pass():
+    """Feeding kvsel_score's own LSE back into kvsel_score_lse reproduces
+    kvsel_score's scores (same data, one pass instead of two)."""
+    wl = get_workload("llama8b_32k_tsp").with_(name="lse_roundtrip", wid=350, n_keys=6000, kv_budget=600,
+                                               tsp_budget=900, n_hubs=60, hidden_dim=None)
+    inp = make_inputs(wl)
+    q = to_dev(inp["q"], wl.dtype)
+    k = to_dev(inp["k"], wl.dtype)
+    lse = torch.empty(inp["q"].shape[:4], dtype=torch.float32, device=device())
+    s2 = K.kvsel_score(q, k, window=wl.window, pool_kernel=wl.pool_kernel, lse_out=lse)
+    s1 = K.kvsel_score_lse(q, k, lse, window=wl.window, pool_kernel=wl.pool_kernel)
+    a, b = s1.cpu().numpy().astype(np.float64), s2.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-30)

@@ -38,6 +38,10 @@ MUTATIONS = {
     "gather_off_by_one": ("out[p] = src[p][idx[p if idx.shape[0] > 1 else 0]]",
                           "out[p] = src[p][np.minimum(idx[p if idx.shape[0] > 1 else 0] + 1, src.shape[1] - 1)]"),
     "bf16_widening": ("(b.astype(np.uint32) << 16)", "(b.astype(np.uint32) << 15)"),
+    "given_lse_sign": ("raw[h // G] += np.exp(logits - lse[h][:, None]).sum(axis=0)",
+                       "raw[h // G] += np.exp(logits + lse[h][:, None]).sum(axis=0)"),
+    "given_lse_no_mean": ("    return raw / G\n\n\ndef saliency_all_given_lse", "    return raw\n\n\ndef saliency_all_given_lse"),
+    "given_lse_wrong_group": ("logits = window_logits(q[h], k[h // G], scale)", "logits = window_logits(q[h], k[h % Hkv], scale)"),
 }
 
 

@@ -73,6 +73,7 @@ void make_geom(const kvsel_score_desc_t* d, ScoreGeom& g, int& RB) {
     g.lse2 = nullptr;
     g.raw = nullptr;
     g.lse_out = nullptr;
+    g.lse_in = nullptr;
 }
 
 ScoreWs ws_layout(const ScoreGeom& g) { return kvsel::score_workspace_layout(g.S, g.n_chunks1, g.Rpad, g.Np); }
@@ -130,33 +131,11 @@ Path choose_path(const Plan& p) {
 
 kvsel_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-const char* kvsel_status_string(kvsel_status_t status) {
-    switch (status) {
-        case KVSEL_OK: return "KVSEL_OK";
-        case KVSEL_ERR_INVALID_ARG: return "KVSEL_ERR_INVALID_ARG: invalid argument";
-        case KVSEL_ERR_UNSUPPORTED: return "KVSEL_ERR_UNSUPPORTED: unsupported head_dim, dtype or pool type";
-        case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE: workspace missing or too small";
-        case KVSEL_ERR_HIP: return "KVSEL_ERR_HIP: HIP runtime error";
-        default: return "KVSEL: unknown status";
-    }
-}
-
-const char* kvsel_version(void) { return "kvsel 0.1.0 (gfx950)"; }
-
-size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc) {
-    if (validate_desc(desc) != KVSEL_OK) return 0;
-    Plan p;
-    make_plan(desc, p);
-    return p.total;
-}
-
-kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
-                           int32_t accumulate, float* lse_out, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+// The scoring call. lse_in == null: both softmax passes (a1-a3). lse_in !=
+// null: the row LSEs are handed in and only the second pass runs.
+kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
+                          int32_t accumulate, float* lse_out, const float* lse_in, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     const kvsel_status_t st = validate_desc(desc);
     if (st != KVSEL_OK) return st;
     if (!q_win || !k || !aligned16(q_win) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
@@ -170,9 +149,11 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
     g.q = q_win;
     g.k = k;
     g.lse_out = lse_out;
+    g.lse_in = lse_in;
     float* raw = nullptr;
     bool done = false;
-    const Path path = choose_path(p);
+    Path path = choose_path(p);
+    if (lse_in && path == Path::Resident) path = p.stream.ok ? Path::Stream : Path::General;
     if (path == Path::Stream) {
         kvsel::StreamArgs a;
         a.q = static_cast<const uint16_t*>(q_win);
@@ -196,7 +177,14 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
         a.part = reinterpret_cast<float2*>(ws + p.stream.part_off);
         a.lse2 = reinterpret_cast<float*>(ws + p.stream.lse2_off);
         a.raw = reinterpret_cast<float*>(ws + p.stream.raw_off);
-        if (kvsel::launch_stream(p.stream, a, lse_out, hs) != hipSuccess) return KVSEL_ERR_HIP;
+        if (lse_in) {
+            if (kvsel::launch_lse_from_input(lse_in, a.lse2, g.S, p.stream.rp, g.R, g.w, g.B, g.Hq, g.Hkv, g.G, hs) !=
+                    hipSuccess ||
+                kvsel::launch_stream_pass2(p.stream, a, hs) != hipSuccess)
+                return KVSEL_ERR_HIP;
+        } else if (kvsel::launch_stream(p.stream, a, lse_out, hs) != hipSuccess) {
+            return KVSEL_ERR_HIP;
+        }
         raw = a.raw;
         done = true;
     }
@@ -250,6 +238,43 @@ kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, co
     }
     return from_hip(kvsel::launch_pool(raw, scores, g.L, (int64_t)g.B * g.Hkv, g.Np, desc->pool_kernel,
                                        accumulate ? 1 : 0, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvsel_status_string(kvsel_status_t status) {
+    switch (status) {
+        case KVSEL_OK: return "KVSEL_OK";
+        case KVSEL_ERR_INVALID_ARG: return "KVSEL_ERR_INVALID_ARG: invalid argument";
+        case KVSEL_ERR_UNSUPPORTED: return "KVSEL_ERR_UNSUPPORTED: unsupported head_dim, dtype or pool type";
+        case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE: workspace missing or too small";
+        case KVSEL_ERR_HIP: return "KVSEL_ERR_HIP: HIP runtime error";
+        default: return "KVSEL: unknown status";
+    }
+}
+
+const char* kvsel_version(void) { return "kvsel 0.1.0 (gfx950)"; }
+
+size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc) {
+    if (validate_desc(desc) != KVSEL_OK) return 0;
+    Plan p;
+    make_plan(desc, p);
+    return p.total;
+}
+
+kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
+                           int32_t accumulate, float* lse_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return score_impl(desc, q_win, k, scores, accumulate, lse_out, nullptr, workspace, workspace_bytes, stream);
+}
+
+kvsel_status_t kvsel_score_lse(const kvsel_score_desc_t* desc, const void* q_win, const void* k, const float* lse_in,
+                               float* scores, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!lse_in) return KVSEL_ERR_INVALID_ARG;
+    return score_impl(desc, q_win, k, scores, accumulate, nullptr, lse_in, workspace, workspace_bytes, stream);
 }
 
 kvsel_status_t kvsel_accumulate(int32_t batch, int32_t n_heads, int64_t n, const float* src, float* dst,

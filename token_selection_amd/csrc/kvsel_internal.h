@@ -27,6 +27,7 @@ struct ScoreGeom {
     float* lse2;      // [S][Rpad] row LSE in the log2 domain (+inf on padded rows)
     float* raw;       // [S][Np] window-summed, group-averaged probabilities
     float* lse_out;   // [L][B][Hq][w] natural-log LSE, or null
+    const float* lse_in;  // [L][B][Hq][w] natural-log LSE handed in (pass 1 skipped), or null
 };
 
 // Workspace layout of the scoring call.
@@ -41,6 +42,11 @@ ScoreWs score_workspace_layout(int64_t S, int64_t n_chunks1, int64_t Rpad, int64
 
 // General path: two launches over K (LSE partials + combine, then scores).
 hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int RB, hipStream_t stream);
+
+// Row LSE2 [S][stride] (log2 domain, +inf past R) from a handed-in natural-log
+// LSE [L][B][Hq][w].
+hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B, int Hq,
+                                 int Hkv, int G, hipStream_t stream);
 
 // Average pool of raw [L][B*Hkv][Np], summed over layers, written or added to scores.
 hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64_t Np, int pool_kernel,
@@ -108,6 +114,8 @@ struct StreamPlan {
 
 bool stream_plan(int dtype, int head_dim, int R, int64_t N, int64_t Np, int64_t S, int n_cu, StreamPlan& plan);
 hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, hipStream_t stream);
+// Pass 2 alone, on row LSEs already in a.lse2.
+hipError_t launch_stream_pass2(const StreamPlan& plan, StreamArgs a, hipStream_t stream);
 
 hipError_t launch_accumulate(int32_t B, int32_t H, int64_t n, const float* src, float* dst, int mode,
                              hipStream_t stream);

@@ -343,10 +343,35 @@ __global__ __launch_bounds__(256) void pool_acc_kernel(const float* __restrict__
     scores[o] = accumulate ? scores[o] + val : val;
 }
 
+// Row LSE2 of every slab from a handed-in natural-log LSE (prefill attention
+// already has it): lse2[s][r] = LSE[l][b][g*G + r/w][r%w] * log2(e) for r < R,
+// +inf (probability 0) on padded rows.
+__global__ void lse_from_input_kernel(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B,
+                                      int Hq, int Hkv, int G) {
+    const int s = blockIdx.y;
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= S || r >= stride) return;
+    float v = INFINITY;
+    if (r < R) {
+        const int kvh = s % Hkv;
+        const int b = (s / Hkv) % B;
+        const int l = s / (Hkv * B);
+        const int h = kvh * G + r / w;
+        const int i = r % w;
+        v = lse_in[(((int64_t)l * B + b) * Hq + h) * w + i] * 1.44269504088896340736f;
+    }
+    lse2[(int64_t)s * stride + r] = v;
+}
+
 template <typename T, int D, int RB>
 void launch_passes(const ScoreGeom& g, hipStream_t st) {
-    hipLaunchKernelGGL((lse_partial_kernel<T, D, RB>), dim3(g.n_chunks1, g.S), dim3(256), 0, st, g);
-    hipLaunchKernelGGL(lse_combine_kernel, dim3((g.Rpad + 255) / 256, g.S), dim3(256), 0, st, g);
+    if (g.lse_in) {
+        hipLaunchKernelGGL(lse_from_input_kernel, dim3((g.Rpad + 255) / 256, g.S), dim3(256), 0, st, g.lse_in, g.lse2,
+                           g.S, g.Rpad, g.R, g.w, g.B, g.Hq, g.Hkv, g.G);
+    } else {
+        hipLaunchKernelGGL((lse_partial_kernel<T, D, RB>), dim3(g.n_chunks1, g.S), dim3(256), 0, st, g);
+        hipLaunchKernelGGL(lse_combine_kernel, dim3((g.Rpad + 255) / 256, g.S), dim3(256), 0, st, g);
+    }
     if (g.Np > 0)
         hipLaunchKernelGGL((raw_score_kernel<T, D, RB>), dim3(g.n_chunks2, g.S), dim3(256), 0, st, g);
 }
@@ -408,6 +433,14 @@ hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int 
         ok = head_dim == 128 ? dispatch_rb<float, 128>(g, RB, st) : dispatch_rb<float, 64>(g, RB, st);
     }
     if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B, int Hq,
+                                 int Hkv, int G, hipStream_t st) {
+    if (S < 1 || S > 65535 || stride < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lse_from_input_kernel, dim3((unsigned)((stride + 255) / 256), (unsigned)S), dim3(256), 0, st,
+                       lse_in, lse2, S, stride, R, w, B, Hq, Hkv, G);
     return hipGetLastError();
 }
 

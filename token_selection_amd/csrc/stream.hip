@@ -385,6 +385,12 @@ hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, h
     hipLaunchKernelGGL(f1, dim3((unsigned)(a.n_seg < plan.n_wg ? a.n_seg : plan.n_wg)), dim3(256), 0, st, a);
     hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.part, plan.spp1, plan.rp, a.R,
                        a.w, a.B, a.Hq, a.Hkv, a.G, a.lse2, lse_out);
+    return launch_stream_pass2(plan, a, st);
+}
+
+hipError_t launch_stream_pass2(const StreamPlan& plan, StreamArgs a, hipStream_t st) {
+    stream_fn f2 = pick(plan.head_dim, plan.rbn_cap, 2);
+    if (!f2) return hipErrorInvalidValue;
     // pass 2 over the prefix keys
     if (a.Np > 0) {
         a.spp = plan.spp2;

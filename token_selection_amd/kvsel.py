@@ -33,6 +33,7 @@ KVSEL_ACC_HEAD_MEAN = 1
 EXPORTED = (
     "kvsel_score_workspace_bytes",
     "kvsel_score",
+    "kvsel_score_lse",
     "kvsel_accumulate",
     "kvsel_topk_workspace_bytes",
     "kvsel_topk",
@@ -86,6 +87,8 @@ def load_library() -> ctypes.CDLL:
     lib.kvsel_score_workspace_bytes.restype = sz
     lib.kvsel_score.argtypes = [ctypes.POINTER(ScoreDesc), vp, vp, vp, i32, vp, vp, sz, vp]
     lib.kvsel_score.restype = i32
+    lib.kvsel_score_lse.argtypes = [ctypes.POINTER(ScoreDesc), vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.kvsel_score_lse.restype = i32
     lib.kvsel_accumulate.argtypes = [i32, i32, i64, vp, vp, i32, vp]
     lib.kvsel_accumulate.restype = i32
     lib.kvsel_topk_workspace_bytes.argtypes = [i32, i32, i64, i32, i32]
@@ -202,6 +205,34 @@ def kvsel_score(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Ten
     st = lib.kvsel_score(ctypes.byref(desc), _ptr(q_win), _ptr(k), _ptr(scores), 1 if accumulate else 0,
                          _ptr(lse_out), _ptr(workspace), workspace.numel(), _stream(dev, stream))
     _check(st, "kvsel_score")
+    return scores
+
+
+def kvsel_score_lse(q_win: torch.Tensor, k: torch.Tensor, lse_in: torch.Tensor,
+                    scores: Optional[torch.Tensor] = None, *, window: int, pool_kernel: int = 7,
+                    accumulate: bool = False, softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                    stream=None, desc: Optional[ScoreDesc] = None) -> torch.Tensor:
+    """As kvsel_score, with the natural-log LSE of every window row handed in
+    (``lse_in``: contiguous float32 [L, B, Hq, w]); only the second softmax
+    pass runs."""
+    lib = load_library()
+    if desc is None:
+        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale)
+    B, Hkv, N, w = desc.batch, desc.n_kv_heads, desc.n_keys, desc.window
+    dev = k.device
+    if scores is None:
+        scores = torch.empty((B, Hkv, N - w), dtype=torch.float32, device=dev)
+    if scores.dtype != torch.float32 or not scores.is_contiguous() or tuple(scores.shape) != (B, Hkv, N - w):
+        raise ValueError("scores must be a contiguous float32 [B, Hkv, N - w] tensor")
+    if (lse_in.dtype != torch.float32 or not lse_in.is_contiguous() or
+            lse_in.numel() != desc.n_layers * B * desc.n_q_heads * w):
+        raise ValueError("lse_in must be a contiguous float32 [L, B, Hq, w] tensor")
+    need = int(lib.kvsel_score_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kvsel_score_lse(ctypes.byref(desc), _ptr(q_win), _ptr(k), _ptr(lse_in), _ptr(scores),
+                             1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    _check(st, "kvsel_score_lse")
     return scores
 
 
