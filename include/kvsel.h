@@ -26,6 +26,7 @@
  *   p[h,i,j]     = exp(logit[h,i,j] - LSE[h,i])                  (row softmax)
  *   raw[g,j]     = (1/G) * sum_{h in group g} sum_{i<w} p[h,i,j]  for j < Np
  *   score[g,j]   = (1/kp) * sum_{t=-r..r} raw[g,j+t]  (raw = 0 outside [0,Np))
+ *                  (KVSEL_POOL_MAX: max_{t=-r..r} raw[g,j+t] inside [0,Np))
  *   C[g,j]       = sum over layers of score[g,j]                  (StructKV)
  *   kept         = the (budget - w) prefix positions of largest score, ties to
  *                  the lower position, plus the window Np .. N-1, ascending.
@@ -52,6 +53,7 @@ typedef int32_t kvsel_status_t;
 #define KVSEL_DTYPE_BF16 1 /* bfloat16 (upper half of a binary32) */
 
 #define KVSEL_POOL_AVG 0 /* stride-1 average pool, zero padded, divisor = kernel */
+#define KVSEL_POOL_MAX 1 /* stride-1 max pool over the positions inside [0, N-w), per layer */
 
 #define KVSEL_ACC_ADD 0       /* dst[b,h,:] += src[b,h,:] */
 #define KVSEL_ACC_HEAD_MEAN 1 /* dst[b,0,:]  = mean over h of src[b,h,:] */
@@ -73,7 +75,7 @@ typedef struct kvsel_score_desc {
     int32_t window;      /* w: 1 <= w <= n_keys */
     int64_t n_keys;      /* N: cached keys per sequence, N < 2^31 */
     int32_t pool_kernel; /* odd, >= 1 (1 = no pool), <= 255 */
-    int32_t pool_type;   /* KVSEL_POOL_AVG */
+    int32_t pool_type;   /* KVSEL_POOL_AVG or KVSEL_POOL_MAX */
     int32_t dtype;       /* KVSEL_DTYPE_F32 or KVSEL_DTYPE_BF16, for Q and K */
     float softmax_scale; /* > 0, or <= 0 for 1/sqrt(head_dim) */
     int64_t q_strides[4];
@@ -162,6 +164,18 @@ size_t kvsel_topk_workspace_bytes(int32_t batch, int32_t rows, int64_t n_keys, i
 kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
                           const float* scores, int32_t* idx, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * kvsel_topk with attention sinks protected (CentroidKV, section 2
+ * inference pipeline: attention sinks and the newest tokens are preserved):
+ * positions 0 .. n_sink-1 are always kept, and they count against the
+ * (budget - window) slots chosen by score. 0 <= n_sink <= budget - window
+ * (and n_sink <= n_keys - window); n_sink = 0 is kvsel_topk. Same workspace
+ * as kvsel_topk. Errors: INVALID_ARG, WORKSPACE, HIP.
+ */
+kvsel_status_t kvsel_topk_sinks(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
+                                int32_t n_sink, const float* scores, int32_t* idx, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Compact the cache (FastKV section 2A: only the kept tokens are passed on;

@@ -241,10 +241,29 @@ def avg_pool(raw_prefix: np.ndarray, kernel: int) -> np.ndarray:
     return out / kernel
 
 
-def pooled_scores(raw: np.ndarray, window: int, kernel: int) -> np.ndarray:
-    """Ranked score of the prefix keys: the pool of raw[..., :N - w]; the
-    window keys are always kept and are neither ranked nor pooled."""
+def max_pool(raw_prefix: np.ndarray, kernel: int) -> np.ndarray:
+    """Stride-1, same-length max pool over the last axis: position j takes the
+    largest value among positions j - r .. j + r that lie inside the row
+    (r = (kernel - 1) / 2). Raw scores are >= 0, so this equals zero padding."""
+    if kernel < 1 or kernel % 2 == 0:
+        raise ValueError("pool kernel must be odd and >= 1")
+    r = (kernel - 1) // 2
+    n = raw_prefix.shape[-1]
+    padded = np.full(raw_prefix.shape[:-1] + (n + 2 * r,), -np.inf)
+    padded[..., r:r + n] = raw_prefix
+    out = np.full(raw_prefix.shape, -np.inf)
+    for tap in range(kernel):
+        out = np.maximum(out, padded[..., tap:tap + n])
+    return out
+
+
+def pooled_scores(raw: np.ndarray, window: int, kernel: int, pool_type: str = "avg") -> np.ndarray:
+    """Ranked score of the prefix keys: the pool of raw[..., :N - w] (average,
+    or with ``pool_type="max"`` the max-pool variant); the window keys are
+    always kept and are neither ranked nor pooled."""
     N = raw.shape[-1]
+    if pool_type == "max":
+        return max_pool(raw[..., :N - window], kernel)
     return avg_pool(raw[..., :N - window], kernel)
 
 
@@ -266,13 +285,15 @@ def head_mean(s: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # select
 # ---------------------------------------------------------------------------
-def select_row(score: np.ndarray, n_keys: int, window: int, budget: int) -> np.ndarray:
+def select_row(score: np.ndarray, n_keys: int, window: int, budget: int, n_sink: int = 0) -> np.ndarray:
     """Kept positions of one selection row.
 
     score: [N - w] prefix scores. The (budget - w) positions with the largest
     score are kept, a tie going to the lower position, then the window
     N - w .. N - 1 is added; the result is sorted ascending (int64, length
-    ``budget``).
+    ``budget``). With ``n_sink`` > 0 the attention sinks 0 .. n_sink-1 are
+    always kept (CentroidKV section 2 preserves sinks and recent tokens) and
+    take n_sink of the (budget - w) slots.
     """
     n_prefix = n_keys - window
     if score.shape[-1] != n_prefix:
@@ -280,17 +301,21 @@ def select_row(score: np.ndarray, n_keys: int, window: int, budget: int) -> np.n
     if not (window <= budget <= n_keys):
         raise ValueError("need window <= budget <= N")
     kk = budget - window
+    if not (0 <= n_sink <= kk):
+        raise ValueError("need 0 <= n_sink <= budget - window")
     pos = np.arange(n_prefix)
     order = np.lexsort((pos, -np.asarray(score, dtype=np.float64)))  # score desc, position asc
+    if n_sink:
+        order = np.concatenate([pos[:n_sink], order[order >= n_sink]])  # sinks first
     kept = np.concatenate([np.sort(order[:kk]), np.arange(n_prefix, n_keys)])
     return kept.astype(np.int64)
 
 
-def select(scores: np.ndarray, n_keys: int, window: int, budget: int) -> np.ndarray:
+def select(scores: np.ndarray, n_keys: int, window: int, budget: int, n_sink: int = 0) -> np.ndarray:
     """select_row over every leading index: [..., N - w] -> [..., budget]."""
     lead = scores.shape[:-1]
     flat = scores.reshape(-1, scores.shape[-1])
-    out = np.stack([select_row(r, n_keys, window, budget) for r in flat]) if flat.shape[0] else \
+    out = np.stack([select_row(r, n_keys, window, budget, n_sink) for r in flat]) if flat.shape[0] else \
         np.zeros((0, budget), dtype=np.int64)
     return out.reshape(lead + (budget,))
 
@@ -317,13 +342,15 @@ def pipeline(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], *, dtype: st
              pool_kernel: int, kv_budget: int, tsp_budget: Optional[int] = None,
              hidden: Optional[np.ndarray] = None, scale: Optional[float] = None,
              threads: int = 1, heads: Optional[Sequence[int]] = None,
-             lse_in: Optional[np.ndarray] = None) -> dict:
+             lse_in: Optional[np.ndarray] = None, pool_type: str = "avg", n_sink: int = 0) -> dict:
     """Score every layer, accumulate over layers (StructKV; a single layer is
     its own sum), select per KV head with the KV budget, and gather K and V of
     every layer with those indices; with a TSP budget also rank the head-mean
     score for one token set per sequence and gather the hidden rows. With
     ``lse_in`` ([L, B, Hq, w] natural-log LSE of the window rows, handed in)
-    the scores use that LSE instead of computing it.
+    the scores use that LSE instead of computing it. ``pool_type`` = "max"
+    takes the max-pool variant; ``n_sink`` protects the first positions in
+    both selections.
 
     Shapes: q [L, B, Hq, w, d]; k, v [L, B, Hkv, N, d]; hidden [B, N, D].
     """
@@ -335,13 +362,13 @@ def pipeline(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], *, dtype: st
     else:
         lse = np.asarray(lse_in, dtype=np.float64)
         raw = saliency_all_given_lse(q, k, lse, dtype, scale, threads=threads)
-    per_layer = pooled_scores(raw, window, pool_kernel)           # [L, B, Hkv, Np]
+    per_layer = pooled_scores(raw, window, pool_kernel, pool_type)  # [L, B, Hkv, Np]
     scores = accumulate_layers(per_layer)                         # [B, Hkv, Np]
     hsel = list(range(Hkv)) if heads is None else list(heads)
     idx = np.zeros((B, Hkv, kv_budget), dtype=np.int64)
     for b in range(B):
         for g in hsel:
-            idx[b, g] = select_row(scores[b, g], N, window, kv_budget)
+            idx[b, g] = select_row(scores[b, g], N, window, kv_budget, n_sink)
     out = {"lse": lse, "raw": raw, "scores": scores, "idx": idx}
     if v is not None:
         kc = np.empty((L, B, Hkv, kv_budget, d), dtype=k.dtype)
@@ -353,7 +380,7 @@ def pipeline(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], *, dtype: st
         out["k_kept"], out["v_kept"] = kc, vc
     if tsp_budget is not None:
         tscore = head_mean(scores)                               # [B, 1, Np]
-        tidx = select(tscore, N, window, tsp_budget)             # [B, 1, budget]
+        tidx = select(tscore, N, window, tsp_budget, n_sink)     # [B, 1, budget]
         out["tsp_scores"], out["tsp_idx"] = tscore, tidx
         if hidden is not None:
             out["hidden_kept"] = np.stack([hidden[b][tidx[b, 0]] for b in range(B)])

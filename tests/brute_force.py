@@ -76,3 +76,19 @@ def brute_select(score, n_keys, window, budget):
     ranked = sorted(range(n_prefix), key=lambda j: (-score[j], j))
     kept = sorted(ranked[: budget - window]) + list(range(n_prefix, n_keys))
     return kept
+
+
+def brute_max_pool(x, kernel):
+    """Max over the positions j - r .. j + r inside the row."""
+    r = (kernel - 1) // 2
+    n = len(x)
+    return [max(x[t] for t in range(max(0, j - r), min(n, j + r + 1))) for j in range(n)]
+
+
+def brute_select_sinks(score, n_keys, window, budget, n_sink):
+    """Positions 0 .. n_sink-1, then the largest (budget - window - n_sink)
+    scores of the other prefix positions (ties to the lower position), plus
+    the window; ascending."""
+    n_prefix = n_keys - window
+    rest = sorted(range(n_sink, n_prefix), key=lambda j: (-score[j], j))
+    return sorted(list(range(n_sink)) + rest[: budget - window - n_sink]) + list(range(n_prefix, n_keys))

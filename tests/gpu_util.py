@@ -52,12 +52,14 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None, lse_in=None):
+def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None, lse_in=None, pool_type=0,
+            n_sink=0):
     """The path as the benchmark runs it: one kvsel_score call over every
     layer, the per-KV-head select, the K/V gather over every layer, and (with
     a TSP budget) head mean, token-set select and hidden gather. With
     ``lse_in`` ([L, B, Hq, w] natural-log LSE) the scoring call is
-    kvsel_score_lse instead."""
+    kvsel_score_lse instead. ``pool_type`` picks the pool (K.KVSEL_POOL_*),
+    ``n_sink`` the protected first positions of both selections."""
     q = to_dev(inp["q"], wl.dtype)
     k = to_dev(inp["k"], wl.dtype)
     L, B, Hq, w, d = inp["q"].shape
@@ -68,13 +70,13 @@ def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None, l
     else:
         scores = torch.full((B, wl.n_kv_heads, wl.n_keys - wl.window), float("nan"), device=device())
     if lse_in is None:
-        K.kvsel_score(q, k, scores, window=wl.window, pool_kernel=wl.pool_kernel,
+        K.kvsel_score(q, k, scores, window=wl.window, pool_kernel=wl.pool_kernel, pool_type=pool_type,
                       accumulate=accumulate_into is not None, lse_out=lse)
     else:
         lse_dev = torch.from_numpy(np.ascontiguousarray(lse_in, dtype=np.float32)).to(device())
         K.kvsel_score_lse(q, k, lse_dev, scores, window=wl.window, pool_kernel=wl.pool_kernel,
-                          accumulate=accumulate_into is not None)
-    idx = K.kvsel_topk(scores, n_keys=wl.n_keys, window=wl.window, budget=wl.kv_budget)
+                          pool_type=pool_type, accumulate=accumulate_into is not None)
+    idx = K.kvsel_topk(scores, n_keys=wl.n_keys, window=wl.window, budget=wl.kv_budget, n_sink=n_sink)
     out["scores"] = scores.cpu().numpy()
     out["idx"] = idx.cpu().numpy()
     if lse is not None:
@@ -86,7 +88,7 @@ def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None, l
         del v
     if wl.tsp_budget is not None:
         tsc = K.kvsel_accumulate(scores, mode=K.KVSEL_ACC_HEAD_MEAN)
-        tidx = K.kvsel_topk(tsc, n_keys=wl.n_keys, window=wl.window, budget=wl.tsp_budget)
+        tidx = K.kvsel_topk(tsc, n_keys=wl.n_keys, window=wl.window, budget=wl.tsp_budget, n_sink=n_sink)
         out["tsp_scores"] = tsc.cpu().numpy()
         out["tsp_idx"] = tidx.cpu().numpy()
         if inp.get("hidden") is not None:
@@ -122,7 +124,7 @@ def assert_lse_close(gpu: np.ndarray, ref: np.ndarray):
 
 
 def assert_selection(idx_gpu: np.ndarray, scores_gpu: np.ndarray, scores_ref: np.ndarray, n_keys: int,
-                     window: int, budget: int, what: str = "idx"):
+                     window: int, budget: int, what: str = "idx", n_sink: int = 0):
     """idx_gpu [..., budget]; scores [..., N - w]."""
     lead = idx_gpu.shape[:-1]
     ig = idx_gpu.reshape(-1, budget).astype(np.int64)
@@ -134,17 +136,18 @@ def assert_selection(idx_gpu: np.ndarray, scores_gpu: np.ndarray, scores_ref: np
         # invariants
         assert np.all(np.diff(row) > 0), f"{what}[{r}] not strictly ascending"
         assert list(row[kk:]) == list(range(n_keys - window, n_keys)), f"{what}[{r}] window not kept last"
+        assert list(row[:n_sink]) == list(range(n_sink)), f"{what}[{r}] sinks not kept"
         # same decision in the same precision: oracle select on the GPU's scores
-        exp_same = oracle.select_row(sg[r], n_keys, window, budget)
+        exp_same = oracle.select_row(sg[r], n_keys, window, budget, n_sink)
         if not np.array_equal(row, exp_same):
             diff = np.setxor1d(row, exp_same)
             raise AssertionError(f"{what}[{r}] differs from the oracle's select of the GPU scores at {diff[:10]}")
         # against the oracle's own scores: only near-threshold positions may differ
-        if kk > 0:
-            exp_ref = oracle.select_row(sr[r], n_keys, window, budget)
+        if kk > n_sink:
+            exp_ref = oracle.select_row(sr[r], n_keys, window, budget, n_sink)
             diff = np.setxor1d(row[:kk], exp_ref[:kk])
             if diff.size:
-                tau = np.sort(sr[r])[::-1][kk - 1]
+                tau = np.sort(sr[r][n_sink:])[::-1][kk - n_sink - 1]
                 far = diff[np.abs(sr[r][diff] - tau) > SCORE_RTOL * abs(tau) + SCORE_ATOL]
                 assert far.size == 0, f"{what}[{r}] differs from the oracle away from the threshold at {far[:10]}"
     return lead
@@ -160,13 +163,14 @@ def assert_gather(kept: np.ndarray, src: np.ndarray, idx: np.ndarray, what: str)
                 raise AssertionError(f"{what}: gathered rows differ at layer {l}, batch {b}")
 
 
-def oracle_for(wl, inp, threads=8, heads=None, lse_in=None):
+def oracle_for(wl, inp, threads=8, heads=None, lse_in=None, pool_type=0, n_sink=0):
     return oracle.pipeline(inp["q"], inp["k"], inp.get("v"), dtype=wl.dtype, window=wl.window,
                            pool_kernel=wl.pool_kernel, kv_budget=wl.kv_budget, tsp_budget=wl.tsp_budget,
-                           hidden=inp.get("hidden"), threads=threads, heads=heads, lse_in=lse_in)
+                           hidden=inp.get("hidden"), threads=threads, heads=heads, lse_in=lse_in,
+                           pool_type="max" if pool_type == K.KVSEL_POOL_MAX else "avg", n_sink=n_sink)
 
 
-def check_all(wl, inp, gpu, ref, heads=None):
+def check_all(wl, inp, gpu, ref, heads=None, n_sink=0):
     """Every comparison of one run (optionally restricted to some KV heads)."""
     hs = list(range(wl.n_kv_heads)) if heads is None else list(heads)
     assert_scores_close(gpu["scores"][:, hs], ref["scores"][:, hs])
@@ -175,14 +179,14 @@ def check_all(wl, inp, gpu, ref, heads=None):
         qh = [h for g in hs for h in range(g * G, (g + 1) * G)]
         assert_lse_close(gpu["lse"][:, :, qh], ref["lse"][:, :, qh])
     assert_selection(gpu["idx"][:, hs], gpu["scores"][:, hs], ref["scores"][:, hs], wl.n_keys, wl.window,
-                     wl.kv_budget)
+                     wl.kv_budget, n_sink=n_sink)
     if "k_kept" in gpu:
         assert_gather(gpu["k_kept"], inp["k"], gpu["idx"], "K")
         assert_gather(gpu["v_kept"], inp["v"], gpu["idx"], "V")
     if wl.tsp_budget is not None and heads is None:
         assert_scores_close(gpu["tsp_scores"], ref["tsp_scores"], "tsp_scores")
         assert_selection(gpu["tsp_idx"], gpu["tsp_scores"], ref["tsp_scores"], wl.n_keys, wl.window,
-                         wl.tsp_budget, "tsp_idx")
+                         wl.tsp_budget, "tsp_idx", n_sink=n_sink)
         if "hidden_kept" in gpu:
             for b in range(wl.batch):
                 exp = inp["hidden"][b][gpu["tsp_idx"][b, 0].astype(np.int64)]

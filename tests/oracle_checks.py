@@ -15,7 +15,8 @@ import math
 import numpy as np
 from scipy.special import logsumexp
 
-from brute_force import brute_pool, brute_saliency, brute_saliency_given_lse, brute_select
+from brute_force import (brute_max_pool, brute_pool, brute_saliency, brute_saliency_given_lse, brute_select,
+                         brute_select_sinks)
 
 # tiny shapes: (Hq, Hkv, w, d, N, pool, budget)
 TINY_CASES = [
@@ -312,7 +313,44 @@ def check_given_lse_mass_and_shift(orc):
                                    rtol=1e-12, atol=1e-300)
 
 
+def check_max_pool(orc):
+    """Max-pool variant: == the brute force on random rows; a lone spike of
+    height h in a zero row becomes h on the 2r+1 positions around it (clipped
+    at the ends) and 0 elsewhere; the pool never lowers a value."""
+    rng = np.random.default_rng(79)
+    for n in (1, 2, 5, 17, 40):
+        for kernel in (1, 3, 5, 7, 9):
+            x = rng.random(n)
+            np.testing.assert_array_equal(orc.max_pool(x, kernel), np.array(brute_max_pool(list(x), kernel)))
+            assert np.all(orc.max_pool(x, kernel) >= x)
+    r, n = 3, 30
+    for p in (0, 1, 14, 28, 29):
+        x = np.zeros(n)
+        x[p] = 2.5
+        exp = np.zeros(n)
+        exp[max(0, p - r):min(n, p + r + 1)] = 2.5
+        np.testing.assert_array_equal(orc.max_pool(x, 2 * r + 1), exp)
+    raw = rng.random((2, 3, 50))
+    np.testing.assert_array_equal(orc.pooled_scores(raw, 6, 5, "max"), orc.max_pool(raw[..., :44], 5))
+
+
+def check_sinks(orc):
+    """Sink protection: == the brute force; every sink is kept even with the
+    lowest scores; n_sink = 0 is the plain select."""
+    rng = np.random.default_rng(80)
+    for (N, w, budget, n_sink) in [(20, 3, 9, 2), (40, 5, 20, 15), (12, 2, 5, 3), (9, 1, 9, 8), (30, 4, 10, 0)]:
+        score = rng.random(N - w)
+        score[:n_sink] = 0.0  # sinks with the lowest scores
+        kept = orc.select_row(score, N, w, budget, n_sink)
+        assert list(kept) == brute_select_sinks(list(score), N, w, budget, n_sink)
+        assert set(range(n_sink)) <= set(kept.tolist())
+        if n_sink == 0:
+            assert list(kept) == brute_select(list(score), N, w, budget)
+
+
 ALL_CHECKS = [
+    check_max_pool,
+    check_sinks,
     check_given_lse_brute,
     check_given_lse_mass_and_shift,
     check_brute_force,

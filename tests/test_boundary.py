@@ -94,7 +94,7 @@ FAKE = 1 << 32  # a 256-byte aligned address that is never dereferenced
     ("window", 0, 1), ("n_keys", 4, 1), ("n_keys", 1 << 31, 1),
     ("pool_kernel", 4, 1), ("pool_kernel", 0, 1), ("pool_kernel", 257, 1),
     ("softmax_scale", float("inf"), 1), ("softmax_scale", float("nan"), 1),
-    ("head_dim", 96, 2), ("dtype", 7, 2), ("pool_type", 1, 2),
+    ("head_dim", 96, 2), ("dtype", 7, 2), ("pool_type", 2, 2),
     ("k_strides", [0, 0, 1024 * 128, 127], 1), ("q_strides", [0, 0, -128, 128], 1),
 ])
 def test_score_rejects_bad_descriptor(lib, field, value, status):
@@ -131,6 +131,18 @@ def test_workspace_grows_with_problem(lib):
 def test_topk_rejects(lib, args):
     B, rows, N, w, budget = args
     assert lib.kvsel_topk(B, rows, N, w, budget, FAKE, FAKE, None, 0, None) == 1
+
+
+@pytest.mark.parametrize("n_sink", [-1, 7, 1 << 20])
+def test_topk_sinks_rejects(lib, n_sink):
+    # window 4, budget 10: at most 6 sinks
+    need = lib.kvsel_topk_workspace_bytes(1, 1, 100, 4, 10)
+    assert lib.kvsel_topk_sinks(1, 1, 100, 4, 10, n_sink, FAKE, FAKE, FAKE, need, None) == 1
+
+
+def test_max_pool_accepted(lib):
+    d = good_desc(pool_type=kvsel.KVSEL_POOL_MAX)
+    assert lib.kvsel_score_workspace_bytes(ctypes.byref(d)) > 0
 
 
 def test_topk_rejects_null(lib):

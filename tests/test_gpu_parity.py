@@ -64,6 +64,73 @@ def test_ragged_shapes(case, path, monkeypatch):
     check_all(wl, inp, gpu, ref)
 
 
+MAXPOOL_CASES = [RAGGED[0], RAGGED[1], RAGGED[6], RAGGED[7], RAGGED[9], RAGGED[10]]
+
+
+@pytest.mark.parametrize("path", ["stream", "resident", "general"])
+@pytest.mark.parametrize("case", MAXPOOL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_max_pool(case, path, monkeypatch):
+    """The max-pool variant on every scoring path: per-layer max over the pool
+    window, then the layer sum (multi-layer cases check that order)."""
+    dt, L, B, Hq, Hkv, d, N, w, pool, budget = case
+    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
+    say("case max-pool", case, path)
+    wl = TINY.with_(name="maxpool", wid=400 + MAXPOOL_CASES.index(case), dtype=dt, n_layers=L, batch=B,
+                    n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool,
+                    kv_budget=budget, n_hubs=min(8, max(0, N - w - 1)))
+    inp = make_inputs(wl)
+    gpu = run_gpu(wl, inp, pool_type=K.KVSEL_POOL_MAX)
+    ref = oracle_for(wl, inp, pool_type=K.KVSEL_POOL_MAX)
+    check_all(wl, inp, gpu, ref)
+
+
+def test_max_pool_given_lse():
+    """Max pool through the single-pass entry point."""
+    wl = TINY.with_(name="maxpool_lse", wid=420, dtype="bf16", head_dim=128, n_layers=2, n_keys=3000, window=16,
+                    kv_budget=300)
+    say("case max-pool given lse")
+    inp = make_inputs(wl)
+    lse = oracle_for(wl, inp)["lse"].astype(np.float32)
+    gpu = run_gpu(wl, inp, lse_in=lse, pool_type=K.KVSEL_POOL_MAX)
+    ref = oracle_for(wl, inp, lse_in=lse.astype(np.float64), pool_type=K.KVSEL_POOL_MAX)
+    check_all(wl, inp, gpu, ref)
+
+
+@pytest.mark.parametrize("n_sink", [1, 4, 37, "all"])
+def test_sinks_are_kept(n_sink):
+    """kvsel_topk_sinks: the first n_sink positions are always kept and the
+    rest of the budget is the top of the other prefix positions, in both the
+    per-KV-head and the token-set selections; "all" fills the whole non-window
+    budget with sinks."""
+    wl = get_workload("llama8b_32k_tsp").with_(name="sinks", wid=430, n_keys=5000, n_hubs=50, hidden_dim=136,
+                                               kv_budget=200, tsp_budget=400)
+    ns = wl.kv_budget - wl.window if n_sink == "all" else n_sink
+    say("case sinks", ns)
+    inp = make_inputs(wl)
+    gpu = run_gpu(wl, inp, n_sink=ns)
+    ref = oracle_for(wl, inp, n_sink=ns)
+    check_all(wl, inp, gpu, ref, n_sink=ns)
+
+
+def test_sinks_with_low_scores():
+    """Sinks whose scores are the lowest of the row (planted through the
+    scores buffer directly) still come first; ties among the others go to the
+    lower position."""
+    B, H, N, w, budget, ns = 2, 3, 4000, 8, 100, 10
+    rng = np.random.default_rng(431)
+    sc = rng.random((B, H, N - w)).astype(np.float32) + 1.0
+    sc[..., :ns] = 0.0
+    sc[..., 500:700] = 2.5  # a tie block larger than the budget
+    say("case sinks low scores")
+    idx = K.kvsel_topk(torch.from_numpy(sc).to(device()), n_keys=N, window=w, budget=budget, n_sink=ns)
+    got = idx.cpu().numpy()
+    exp = list(range(ns)) + list(range(500, 500 + budget - w - ns)) + list(range(N - w, N))
+    for b in range(B):
+        for h in range(H):
+            assert got[b, h].tolist() == exp
+            assert got[b, h].tolist() == oracle.select_row(sc[b, h].astype(np.float64), N, w, budget, ns).tolist()
+
+
 def test_rope_sink_tsp_small():
     """The token-set (TSP) path on a reduced 32K-style layer: RoPE, a sink,
     hubs, head mean, one token set per sequence, hidden-row gather."""

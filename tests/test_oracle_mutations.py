@@ -38,6 +38,11 @@ MUTATIONS = {
     "gather_off_by_one": ("out[p] = src[p][idx[p if idx.shape[0] > 1 else 0]]",
                           "out[p] = src[p][np.minimum(idx[p if idx.shape[0] > 1 else 0] + 1, src.shape[1] - 1)]"),
     "bf16_widening": ("(b.astype(np.uint32) << 16)", "(b.astype(np.uint32) << 15)"),
+    "max_pool_dropped_tap": ("for tap in range(kernel):", "for tap in range(kernel - 1):"),
+    "max_pool_as_avg": ("        return max_pool(raw[..., :N - window], kernel)", "        return avg_pool(raw[..., :N - window], kernel)"),
+    "sinks_dropped": ("        order = np.concatenate([pos[:n_sink], order[order >= n_sink]])  # sinks first", "        pass"),
+    "sinks_off_by_one": ("        order = np.concatenate([pos[:n_sink], order[order >= n_sink]])  # sinks first",
+                         "        order = np.concatenate([pos[:n_sink - 1], order[order >= n_sink - 1]])"),
     "given_lse_sign": ("raw[h // G] += np.exp(logits - lse[h][:, None]).sum(axis=0)",
                        "raw[h // G] += np.exp(logits + lse[h][:, None]).sum(axis=0)"),
     "given_lse_no_mean": ("    return raw / G\n\n\ndef saliency_all_given_lse", "    return raw\n\n\ndef saliency_all_given_lse"),

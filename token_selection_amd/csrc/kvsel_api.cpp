@@ -35,7 +35,7 @@ kvsel_status_t validate_desc(const kvsel_score_desc_t* d) {
         if (d->q_strides[i] < 0 || d->k_strides[i] < 0) return KVSEL_ERR_INVALID_ARG;
     if (d->dtype != KVSEL_DTYPE_F32 && d->dtype != KVSEL_DTYPE_BF16) return KVSEL_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
-    if (d->pool_type != KVSEL_POOL_AVG) return KVSEL_ERR_UNSUPPORTED;
+    if (d->pool_type != KVSEL_POOL_AVG && d->pool_type != KVSEL_POOL_MAX) return KVSEL_ERR_UNSUPPORTED;
     const int64_t e = d->dtype == KVSEL_DTYPE_F32 ? 4 : 2;
     for (int i = 0; i < 4; ++i)
         if ((d->q_strides[i] * e) % 16 != 0 || (d->k_strides[i] * e) % 16 != 0) return KVSEL_ERR_INVALID_ARG;
@@ -237,7 +237,7 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         raw = g.raw;
     }
     return from_hip(kvsel::launch_pool(raw, scores, g.L, (int64_t)g.B * g.Hkv, g.Np, desc->pool_kernel,
-                                       accumulate ? 1 : 0, hs));
+                                       desc->pool_type, accumulate ? 1 : 0, hs));
 }
 
 }  // namespace
@@ -290,16 +290,23 @@ size_t kvsel_topk_workspace_bytes(int32_t batch, int32_t rows, int64_t n_keys, i
     return kvsel::topk_workspace_bytes(batch * rows, n_keys - window);
 }
 
-kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
-                          const float* scores, int32_t* idx, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+kvsel_status_t kvsel_topk_sinks(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
+                                int32_t n_sink, const float* scores, int32_t* idx, void* workspace,
+                                size_t workspace_bytes, void* stream) {
     if (batch < 1 || rows < 1 || (int64_t)batch * rows > 65535) return KVSEL_ERR_INVALID_ARG;
     if (window < 1 || budget < window || n_keys < budget || n_keys >= kMaxKeys) return KVSEL_ERR_INVALID_ARG;
+    if (n_sink < 0 || n_sink > budget - window) return KVSEL_ERR_INVALID_ARG;
     if (!idx || (n_keys > window && !scores)) return KVSEL_ERR_INVALID_ARG;
     const size_t need = kvsel::topk_workspace_bytes(batch * rows, n_keys - window);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
-    return from_hip(kvsel::launch_topk(batch * rows, n_keys, window, budget, scores, idx, workspace,
+    return from_hip(kvsel::launch_topk(batch * rows, n_keys, window, budget, n_sink, scores, idx, workspace,
                                        static_cast<hipStream_t>(stream)));
+}
+
+kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
+                          const float* scores, int32_t* idx, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return kvsel_topk_sinks(batch, rows, n_keys, window, budget, 0, scores, idx, workspace, workspace_bytes, stream);
 }
 
 kvsel_status_t kvsel_gather(int32_t n_layers, int32_t batch, int32_t n_heads, int32_t idx_heads, int32_t budget,

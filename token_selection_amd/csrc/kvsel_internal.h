@@ -48,8 +48,9 @@ hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int 
 hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B, int Hq,
                                  int Hkv, int G, hipStream_t stream);
 
-// Average pool of raw [L][B*Hkv][Np], summed over layers, written or added to scores.
-hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64_t Np, int pool_kernel,
+// Pool (KVSEL_POOL_AVG or _MAX) of raw [L][B*Hkv][Np], summed over layers,
+// written or added to scores.
+hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64_t Np, int pool_kernel, int pool_type,
                        int accumulate, hipStream_t stream);
 
 // Register-resident path (bf16): one cooperative launch reads K once.
@@ -121,8 +122,8 @@ hipError_t launch_accumulate(int32_t B, int32_t H, int64_t n, const float* src, 
                              hipStream_t stream);
 
 size_t topk_workspace_bytes(int32_t rows, int64_t n_prefix);
-hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, const float* scores,
-                       int32_t* idx, void* workspace, hipStream_t stream);
+hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, int32_t n_sink,
+                       const float* scores, int32_t* idx, void* workspace, hipStream_t stream);
 
 hipError_t launch_gather(int32_t L, int32_t B, int32_t H, int32_t idx_heads, int32_t budget, int64_t n_src_rows,
                          int64_t row_bytes, const void* src, const int64_t s[4], const int32_t* idx, void* dst,

@@ -12,7 +12,8 @@
 //           window row in the log2 domain; lse_combine_kernel merges chunks.
 //   pass 2  raw_score_kernel: recompute the logits, exp2(x - LSE2) and sum
 //           them per key over all G*w rows of the KV head.
-//   then    pool_acc_kernel: the average pool, summed over layers.
+//   then    pool_acc_kernel: the average pool, summed over layers (or
+//           pool_max_acc_kernel: the max pool of each layer, summed).
 //
 // Logits come from v_mfma_f32_16x16x32_bf16 (bf16 inputs) or
 // v_mfma_f32_16x16x4_f32 (fp32 inputs) with fp32 accumulation. The window
@@ -343,6 +344,36 @@ __global__ __launch_bounds__(256) void pool_acc_kernel(const float* __restrict__
     scores[o] = accumulate ? scores[o] + val : val;
 }
 
+// Max pool variant: s[j] = max over t = -r..r of raw[j + t], positions outside
+// [0, Np) left out (scores are >= 0, so this equals zero padding). A max does
+// not commute with the sum over layers, so each layer is pooled on its own and
+// the pooled layers are added up.
+__global__ __launch_bounds__(256) void pool_max_acc_kernel(const float* __restrict__ raw, float* __restrict__ scores,
+                                                           int L, int64_t BH, int64_t Np, int kern, int accumulate) {
+    __shared__ float tile[kPoolTile + 2 * kPoolMaxR];
+    const int64_t bh = blockIdx.y;
+    const int64_t j0 = (int64_t)blockIdx.x * kPoolTile;
+    const int r = (kern - 1) / 2;
+    const int span = kPoolTile + 2 * r;
+    const int64_t j = j0 + threadIdx.x;
+    float acc = 0.f;
+    for (int l = 0; l < L; ++l) {
+        const float* p = raw + ((int64_t)l * BH + bh) * Np;
+        __syncthreads();  // the previous layer's tile has been read
+        for (int t = threadIdx.x; t < span; t += 256) {
+            const int64_t jj = j0 - r + t;
+            tile[t] = (jj >= 0 && jj < Np) ? p[jj] : -INFINITY;
+        }
+        __syncthreads();
+        float m = -INFINITY;
+        for (int t = 0; t < kern; ++t) m = fmaxf(m, tile[threadIdx.x + t]);
+        acc += m;
+    }
+    if (j >= Np) return;
+    const int64_t o = bh * Np + j;
+    scores[o] = accumulate ? scores[o] + acc : acc;
+}
+
 // Row LSE2 of every slab from a handed-in natural-log LSE (prefill attention
 // already has it): lse2[s][r] = LSE[l][b][g*G + r/w][r%w] * log2(e) for r < R,
 // +inf (probability 0) on padded rows.
@@ -445,11 +476,15 @@ hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int st
 }
 
 hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64_t Np, int pool_kernel,
-                       int accumulate, hipStream_t st) {
+                       int pool_type, int accumulate, hipStream_t st) {
     if (Np <= 0) return hipSuccess;
     if ((pool_kernel - 1) / 2 > kPoolMaxR || BH > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pool_acc_kernel, dim3((unsigned)((Np + kPoolTile - 1) / kPoolTile), (unsigned)BH), dim3(256), 0,
-                       st, raw, scores, L, BH, Np, pool_kernel, accumulate);
+    const dim3 grid((unsigned)((Np + kPoolTile - 1) / kPoolTile), (unsigned)BH);
+    if (pool_type == KVSEL_POOL_MAX)
+        hipLaunchKernelGGL(pool_max_acc_kernel, grid, dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel,
+                           accumulate);
+    else
+        hipLaunchKernelGGL(pool_acc_kernel, grid, dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel, accumulate);
     return hipGetLastError();
 }
 

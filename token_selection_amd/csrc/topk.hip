@@ -46,11 +46,19 @@ __device__ __forceinline__ uint32_t order_key(uint32_t u) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Rank key of prefix position i of a row: protected sink positions take the
+// largest key (above +inf's), so the select keeps them and orders them by
+// position like any other tie.
+__device__ __forceinline__ uint32_t rank_key(const uint32_t* x, int64_t i, int32_t n_sink) {
+    return i < n_sink ? 0xFFFFFFFFu : order_key(x[i]);
+}
+
 struct TopkGeom {
     const uint32_t* x;  // scores as bits [rows][Np]
     int32_t* idx;       // [rows][budget]
     int64_t Np;
     int32_t w, budget, kk;
+    int32_t n_sink;     // positions 0 .. n_sink-1 rank above every score (always kept)
     int32_t chunks;     // chunks per row
     int64_t chunk_len;  // elements per chunk (the last one may be shorter)
     uint32_t* hist;     // [rows][kPasses][kBins], zeroed by the window kernel
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkGeom g, int pas
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int64_t i = i0 + threadIdx.x + (int64_t)k * kThreads;
-            u[k] = i < e ? order_key(x[i]) : 0u;
+            u[k] = i < e ? rank_key(x, i, g.n_sink) : 0u;
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void topk_count_kernel(TopkGeom g) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int64_t i = i0 + threadIdx.x + (int64_t)k * kThreads;
-            u[k] = i < e ? order_key(x[i]) : 0u;
+            u[k] = i < e ? rank_key(x, i, g.n_sink) : 0u;
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkGeom g) {
         uint32_t u[PER];
         const int64_t first = t0 + (int64_t)tid * PER;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) u[k] = first + k < e ? order_key(x[first + k]) : 0u;
+        for (int k = 0; k < PER; ++k) u[k] = first + k < e ? rank_key(x, first + k, g.n_sink) : 0u;
         uint32_t cgt = 0u, ceq = 0u;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
@@ -319,10 +327,11 @@ size_t topk_workspace_bytes(int32_t rows, int64_t Np) {
            align256((size_t)rows * chunks * 2 * sizeof(uint32_t));
 }
 
-hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, const float* scores,
-                       int32_t* idx, void* ws, hipStream_t st) {
+hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, int32_t n_sink,
+                       const float* scores, int32_t* idx, void* ws, hipStream_t st) {
     const int64_t Np = n_keys - window;
     TopkGeom g;
+    g.n_sink = n_sink;
     g.x = reinterpret_cast<const uint32_t*>(scores);
     g.idx = idx;
     g.Np = Np;

@@ -27,6 +27,7 @@ KVSEL_ERR_HIP = 4
 KVSEL_DTYPE_F32 = 0
 KVSEL_DTYPE_BF16 = 1
 KVSEL_POOL_AVG = 0
+KVSEL_POOL_MAX = 1
 KVSEL_ACC_ADD = 0
 KVSEL_ACC_HEAD_MEAN = 1
 
@@ -37,6 +38,7 @@ EXPORTED = (
     "kvsel_accumulate",
     "kvsel_topk_workspace_bytes",
     "kvsel_topk",
+    "kvsel_topk_sinks",
     "kvsel_gather",
     "kvsel_status_string",
     "kvsel_version",
@@ -95,6 +97,8 @@ def load_library() -> ctypes.CDLL:
     lib.kvsel_topk_workspace_bytes.restype = sz
     lib.kvsel_topk.argtypes = [i32, i32, i64, i32, i32, vp, vp, vp, sz, vp]
     lib.kvsel_topk.restype = i32
+    lib.kvsel_topk_sinks.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.kvsel_topk_sinks.restype = i32
     lib.kvsel_gather.argtypes = [i32, i32, i32, i32, i32, i64, i64, vp, ctypes.POINTER(ctypes.c_int64), vp, vp, vp]
     lib.kvsel_gather.restype = i32
     lib.kvsel_status_string.argtypes = [i32]
@@ -154,7 +158,7 @@ def _as5(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def score_desc(q_win: torch.Tensor, k: torch.Tensor, window: int, pool_kernel: int = 7,
-               softmax_scale: float = 0.0) -> ScoreDesc:
+               softmax_scale: float = 0.0, pool_type: int = 0) -> ScoreDesc:
     q5, k5 = _as5(q_win, "q_win"), _as5(k, "k")
     L, B, Hq, w, d = q5.shape
     Lk, Bk, Hkv, N, dk = k5.shape
@@ -165,7 +169,7 @@ def score_desc(q_win: torch.Tensor, k: torch.Tensor, window: int, pool_kernel: i
     desc = ScoreDesc()
     desc.n_layers, desc.batch, desc.n_q_heads, desc.n_kv_heads = L, B, Hq, Hkv
     desc.head_dim, desc.window, desc.n_keys = d, window, N
-    desc.pool_kernel, desc.pool_type = pool_kernel, KVSEL_POOL_AVG
+    desc.pool_kernel, desc.pool_type = pool_kernel, int(pool_type)
     desc.dtype = _dtype_code(q5.dtype)
     if k5.dtype != q5.dtype:
         raise ValueError("q_win and k must share a dtype")
@@ -183,13 +187,13 @@ def kvsel_score_workspace_bytes(desc: ScoreDesc) -> int:
 def kvsel_score(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Tensor] = None, *, window: int,
                 pool_kernel: int = 7, accumulate: bool = False, lse_out: Optional[torch.Tensor] = None,
                 softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None,
-                desc: Optional[ScoreDesc] = None) -> torch.Tensor:
+                desc: Optional[ScoreDesc] = None, pool_type: int = 0) -> torch.Tensor:
     """Saliency scores [B, Hkv, N - w] (fp32), summed over the L layers of the
     call (added to ``scores`` when ``accumulate``). ``q_win``: [L, B, Hq, w, d]
     or [B, Hq, w, d]; ``k``: [L, B, Hkv, N, d] or [B, Hkv, N, d]; bf16 or fp32."""
     lib = load_library()
     if desc is None:
-        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale)
+        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type)
     B, Hkv, N, w = desc.batch, desc.n_kv_heads, desc.n_keys, desc.window
     dev = k.device
     if scores is None:
@@ -211,13 +215,13 @@ def kvsel_score(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Ten
 def kvsel_score_lse(q_win: torch.Tensor, k: torch.Tensor, lse_in: torch.Tensor,
                     scores: Optional[torch.Tensor] = None, *, window: int, pool_kernel: int = 7,
                     accumulate: bool = False, softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
-                    stream=None, desc: Optional[ScoreDesc] = None) -> torch.Tensor:
+                    stream=None, desc: Optional[ScoreDesc] = None, pool_type: int = 0) -> torch.Tensor:
     """As kvsel_score, with the natural-log LSE of every window row handed in
     (``lse_in``: contiguous float32 [L, B, Hq, w]); only the second softmax
     pass runs."""
     lib = load_library()
     if desc is None:
-        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale)
+        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type)
     B, Hkv, N, w = desc.batch, desc.n_kv_heads, desc.n_keys, desc.window
     dev = k.device
     if scores is None:
@@ -266,9 +270,10 @@ def kvsel_topk_workspace_bytes(batch: int, rows: int, n_keys: int, window: int, 
 
 
 def kvsel_topk(scores: torch.Tensor, *, n_keys: int, window: int, budget: int, idx: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+               workspace: Optional[torch.Tensor] = None, stream=None, n_sink: int = 0) -> torch.Tensor:
     """Kept positions [B, rows, budget] (int32, ascending, window last) of
-    scores [B, rows, N - w]."""
+    scores [B, rows, N - w]; with ``n_sink`` > 0 positions 0 .. n_sink-1 are
+    always kept (kvsel_topk_sinks)."""
     lib = load_library()
     if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be a contiguous float32 [B, rows, N - w] tensor")
@@ -283,8 +288,12 @@ def kvsel_topk(scores: torch.Tensor, *, n_keys: int, window: int, budget: int, i
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check(lib.kvsel_topk(B, rows, n_keys, window, budget, _ptr(scores), _ptr(idx), _ptr(workspace), ws_bytes,
-                          _stream(scores.device, stream)), "kvsel_topk")
+    if n_sink:
+        _check(lib.kvsel_topk_sinks(B, rows, n_keys, window, budget, n_sink, _ptr(scores), _ptr(idx),
+                                    _ptr(workspace), ws_bytes, _stream(scores.device, stream)), "kvsel_topk_sinks")
+    else:
+        _check(lib.kvsel_topk(B, rows, n_keys, window, budget, _ptr(scores), _ptr(idx), _ptr(workspace), ws_bytes,
+                              _stream(scores.device, stream)), "kvsel_topk")
     return idx
 
 
