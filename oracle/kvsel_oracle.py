@@ -224,6 +224,100 @@ class _null:
 
 
 # ---------------------------------------------------------------------------
+# pivot statistics (StructKV section 2, dynamic pivot detection)
+# ---------------------------------------------------------------------------
+def row_stats(q: np.ndarray, k: np.ndarray, small_p: float, scale: Optional[float] = None):
+    """Attention statistics of every window row of one (layer, sequence).
+
+    StructKV section 2 watches attention entropy, sparsity and variance during
+    the first pass and looks for the layer where entropy falls and sparsity
+    rises. Row i of head h has the distribution p_j = exp(l_j - LSE) over the
+    keys it sees (j <= N - w + i, n_i = N - w + i + 1 of them):
+
+        entropy = -sum_j p_j ln p_j                  (nats)
+        sum_p2  = sum_j p_j^2                        (the row's variance is
+                                                      sum_p2 / n_i - 1 / n_i^2)
+        n_below = number of visible j with p_j < small_p   (sparsity = n_below / n_i)
+
+    q: [Hq, w, d], k: [Hkv, N, d] float64. Returns (entropy [Hq, w],
+    sum_p2 [Hq, w], n_below [Hq, w] int64).
+    """
+    Hq, w, d = q.shape
+    Hkv, N, _ = k.shape
+    G = Hq // Hkv
+    scale = default_scale(d) if scale is None else scale
+    entropy = np.empty((Hq, w))
+    sum_p2 = np.empty((Hq, w))
+    n_below = np.empty((Hq, w), dtype=np.int64)
+    for h in range(Hq):
+        g = h // G  # the KV head this query head reads
+        logits = window_logits(q[h], k[g], scale)
+        visible = np.isfinite(logits)
+        logp = np.where(visible, logits - row_lse(logits)[:, None], 0.0)
+        p = np.where(visible, np.exp(logp), 0.0)
+        entropy[h] = -(p * logp).sum(axis=1)
+        sum_p2[h] = (p * p).sum(axis=1)
+        n_below[h] = (visible & (p < small_p)).sum(axis=1)
+    return entropy, sum_p2, n_below
+
+
+def row_stats_all(q: np.ndarray, k: np.ndarray, dtype: str, small_p: float, scale: Optional[float] = None,
+                  threads: int = 1):
+    """row_stats over every (layer, sequence): q [L, B, Hq, w, d], k [L, B, Hkv,
+    N, d] in the stored element type -> (entropy, sum_p2, n_below), each
+    [L, B, Hq, w]."""
+    L, B, Hq, w, _ = q.shape
+    ent = np.full((L, B, Hq, w), np.nan)
+    sp2 = np.full((L, B, Hq, w), np.nan)
+    nb = np.zeros((L, B, Hq, w), dtype=np.int64)
+
+    def unit(args):
+        l, b = args
+        ent[l, b], sp2[l, b], nb[l, b] = row_stats(to_f64(q[l, b], dtype), to_f64(k[l, b], dtype), small_p, scale)
+
+    jobs = [(l, b) for l in range(L) for b in range(B)]
+    if threads <= 1:
+        for j in jobs:
+            unit(j)
+    else:
+        ctx = threadpool_limits(1) if threadpool_limits is not None else _null()
+        with ctx, cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(unit, jobs))
+    return ent, sp2, nb
+
+
+def layer_summary(entropy: np.ndarray, sum_p2: np.ndarray, n_below: np.ndarray, n_keys: int):
+    """Per-layer means over (sequence, head, window row) of the row entropy,
+    the sparsity n_below / n_i and the variance sum_p2 / n_i - 1 / n_i^2.
+    Inputs [L, B, Hq, w]; returns three [L] arrays."""
+    w = entropy.shape[-1]
+    n = (n_keys - w + 1 + np.arange(w)).astype(np.float64)  # keys row i sees
+    ent = entropy.reshape(entropy.shape[0], -1, w)
+    spars = (n_below / n).reshape(ent.shape)
+    var = (sum_p2 / n - 1.0 / (n * n)).reshape(ent.shape)
+    return ent.mean(axis=(1, 2)), spars.mean(axis=(1, 2)), var.mean(axis=(1, 2))
+
+
+def pivot_layer(mean_entropy: Sequence[float], mean_sparsity: Sequence[float], min_drop: float,
+                min_rise: float) -> int:
+    """StructKV's pivot: the first layer l >= 1 at which the attention pattern
+    changes phase, read as the mean entropy falling by at least ``min_drop``
+    (a fraction of layer l-1's entropy) while the mean sparsity rises by at
+    least ``min_rise`` (an absolute fraction), both against layer l-1. Layers
+    0 .. pivot are accumulated. Without such a layer the pivot is the last
+    layer."""
+    L = len(mean_entropy)
+    if L < 1 or len(mean_sparsity) != L:
+        raise ValueError("need one entropy and one sparsity value per layer")
+    for l in range(1, L):
+        fell = mean_entropy[l - 1] - mean_entropy[l] >= min_drop * mean_entropy[l - 1]
+        rose = mean_sparsity[l] - mean_sparsity[l - 1] >= min_rise
+        if fell and rose:
+            return l
+    return L - 1
+
+
+# ---------------------------------------------------------------------------
 # pool, accumulate
 # ---------------------------------------------------------------------------
 def avg_pool(raw_prefix: np.ndarray, kernel: int) -> np.ndarray:

@@ -92,3 +92,24 @@ def brute_select_sinks(score, n_keys, window, budget, n_sink):
     n_prefix = n_keys - window
     rest = sorted(range(n_sink, n_prefix), key=lambda j: (-score[j], j))
     return sorted(list(range(n_sink)) + rest[: budget - window - n_sink]) + list(range(n_prefix, n_keys))
+
+
+def brute_row_stats(q, k, scale, small_p):
+    """Per window row: entropy -sum p ln p, sum p^2 and the count of visible
+    keys with p < small_p, by explicit loops (q [Hq][w][d], k [Hkv][N][d])."""
+    Hq, w, d = len(q), len(q[0]), len(q[0][0])
+    Hkv, N = len(k), len(k[0])
+    G = Hq // Hkv
+    ent = [[0.0] * w for _ in range(Hq)]
+    sp2 = [[0.0] * w for _ in range(Hq)]
+    nb = [[0] * w for _ in range(Hq)]
+    for h in range(Hq):
+        for i in range(w):
+            logit = [scale * math.fsum(q[h][i][t] * k[h // G][j][t] for t in range(d)) for j in range(N - w + i + 1)]
+            top = max(logit)
+            total = math.fsum(math.exp(x - top) for x in logit)
+            probs = [math.exp(x - top) / total for x in logit]
+            ent[h][i] = -math.fsum(pj * math.log(pj) for pj in probs if pj > 0.0)
+            sp2[h][i] = math.fsum(pj * pj for pj in probs)
+            nb[h][i] = sum(1 for pj in probs if pj < small_p)
+    return ent, sp2, nb

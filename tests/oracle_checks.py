@@ -15,8 +15,8 @@ import math
 import numpy as np
 from scipy.special import logsumexp
 
-from brute_force import (brute_max_pool, brute_pool, brute_saliency, brute_saliency_given_lse, brute_select,
-                         brute_select_sinks)
+from brute_force import (brute_max_pool, brute_pool, brute_row_stats, brute_saliency, brute_saliency_given_lse,
+                         brute_select, brute_select_sinks)
 
 # tiny shapes: (Hq, Hkv, w, d, N, pool, budget)
 TINY_CASES = [
@@ -348,7 +348,83 @@ def check_sinks(orc):
             assert list(kept) == brute_select(list(score), N, w, budget)
 
 
+def check_row_stats_brute(orc):
+    """Row statistics == explicit loops on tiny shapes (G = 2, causal rows of
+    different lengths), with the threshold between the rows' probabilities."""
+    rng = np.random.default_rng(91)
+    for (Hq, Hkv, w, N, d, tau) in [(2, 1, 3, 7, 4, 0.1), (4, 2, 4, 9, 3, 0.05), (3, 3, 1, 5, 2, 0.3)]:
+        q = rng.normal(size=(Hq, w, d)) * 1.5
+        k = rng.normal(size=(Hkv, N, d))
+        ent, sp2, nb = orc.row_stats(q, k, tau)
+        bent, bsp2, bnb = brute_row_stats(q.tolist(), k.tolist(), 1.0 / math.sqrt(d), tau)
+        np.testing.assert_allclose(ent, np.array(bent), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(sp2, np.array(bsp2), rtol=1e-12, atol=1e-14)
+        assert nb.tolist() == bnb
+
+
+def check_row_stats_closed_forms(orc):
+    """q = 0: every row is uniform over its n_i visible keys, so entropy =
+    ln n_i, sum p^2 = 1 / n_i, and n_below is n_i or 0 as the threshold lies
+    above or below 1 / n_i. A dominant key: entropy -> 0 and sum p^2 -> 1.
+    scipy.stats.entropy on one row. Bounds: -ln sum p^2 <= entropy <= ln n_i."""
+    from scipy.stats import entropy as sp_entropy
+
+    N, w, d = 40, 5, 8
+    k = np.random.default_rng(92).normal(size=(2, N, d))
+    n = N - w + 1 + np.arange(w)
+    q = np.zeros((4, w, d))
+    for tau, full in ((1.0 / (N - w + 1) + 1e-3, True), (1.0 / N - 1e-3, False)):
+        ent, sp2, nb = orc.row_stats(q, k, tau)
+        np.testing.assert_allclose(ent, np.broadcast_to(np.log(n), ent.shape), rtol=1e-13)
+        np.testing.assert_allclose(sp2, np.broadcast_to(1.0 / n, sp2.shape), rtol=1e-12)
+        assert (nb == (n if full else 0)).all()
+    kd = np.zeros((1, N, d))
+    kd[0, 3, 0] = 400.0
+    qd = np.zeros((1, w, d))
+    qd[0, :, 0] = 1.0
+    ent, sp2, nb = orc.row_stats(qd, kd, 0.5)
+    assert (ent < 1e-30 + 1e-10).all() and np.allclose(sp2, 1.0) and (nb == n - 1).all()
+    rng = np.random.default_rng(93)
+    q = rng.normal(size=(4, w, d)) * 2.0
+    ent, sp2, nb = orc.row_stats(q, k, 1e-3)
+    logits = orc.window_logits(q[1], k[0], 1.0 / math.sqrt(d))
+    pr = np.exp(logits[2] - logits[2][np.isfinite(logits[2])].max())
+    pr = pr[np.isfinite(logits[2])]
+    assert abs(ent[1, 2] - sp_entropy(pr / pr.sum())) < 1e-12
+    assert (ent <= np.log(n) + 1e-12).all() and (-np.log(sp2) <= ent + 1e-12).all()
+
+
+def check_layer_summary_and_pivot(orc):
+    """layer_summary of uniform rows: entropy ln n, sparsity 1 or 0, variance
+    0. pivot_layer on hand-made sequences: the first layer where both the
+    relative entropy fall and the sparsity rise reach their thresholds; a fall
+    alone or a rise alone is no pivot; none -> the last layer."""
+    L, B, Hq, w, N = 3, 1, 2, 4, 20
+    n = N - w + 1 + np.arange(w)
+    ent = np.broadcast_to(np.log(n), (L, B, Hq, w)).copy()
+    sp2 = np.broadcast_to(1.0 / n, (L, B, Hq, w)).copy()
+    nb = np.broadcast_to(n, (L, B, Hq, w)).copy()
+    nb[1] = 0
+    me, ms, mv = orc.layer_summary(ent, sp2, nb, N)
+    np.testing.assert_allclose(me, np.log(n).mean())
+    np.testing.assert_allclose(ms, [1.0, 0.0, 1.0])
+    np.testing.assert_allclose(mv, 0.0, atol=1e-15)
+    E = [10.0, 9.9, 9.8, 6.0, 5.9, 2.0]
+    S = [0.10, 0.10, 0.12, 0.50, 0.52, 0.90]
+    assert orc.pivot_layer(E, S, 0.1, 0.05) == 3
+    assert orc.pivot_layer(E, S, 0.5, 0.05) == 5
+    assert orc.pivot_layer(E, [0.1] * 6, 0.1, 0.05) == 5     # entropy falls, sparsity flat
+    assert orc.pivot_layer([5.0] * 6, S, 0.1, 0.05) == 5     # sparsity rises, entropy flat
+    assert orc.pivot_layer([10.0, 9.0, 8.9], [0.1, 0.3, 0.31], 0.05, 0.1) == 1
+    assert orc.pivot_layer([10.0, 10.0, 5.0, 5.0], [0.0, 0.0, 0.5, 0.5], 0.1, 0.1) == 2
+    assert orc.pivot_layer([10.0, 12.0, 5.0], [0.5, 0.0, 0.5], 0.1, 0.1) == 2  # rises are against l - 1
+    assert orc.pivot_layer([7.0], [0.3], 0.1, 0.05) == 0
+
+
 ALL_CHECKS = [
+    check_row_stats_brute,
+    check_row_stats_closed_forms,
+    check_layer_summary_and_pivot,
     check_max_pool,
     check_sinks,
     check_given_lse_brute,

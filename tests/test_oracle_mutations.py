@@ -43,6 +43,16 @@ MUTATIONS = {
     "sinks_dropped": ("        order = np.concatenate([pos[:n_sink], order[order >= n_sink]])  # sinks first", "        pass"),
     "sinks_off_by_one": ("        order = np.concatenate([pos[:n_sink], order[order >= n_sink]])  # sinks first",
                          "        order = np.concatenate([pos[:n_sink - 1], order[order >= n_sink - 1]])"),
+    "stats_wrong_group": ("        g = h // G  # the KV head this query head reads", "        g = h % Hkv"),
+    "stats_entropy_sign": ("        entropy[h] = -(p * logp).sum(axis=1)", "        entropy[h] = (p * logp).sum(axis=1)"),
+    "stats_p2_unsquared": ("        sum_p2[h] = (p * p).sum(axis=1)", "        sum_p2[h] = p.sum(axis=1)"),
+    "stats_count_masked": ("        n_below[h] = (visible & (p < small_p)).sum(axis=1)", "        n_below[h] = (p < small_p).sum(axis=1)"),
+    "stats_count_above": ("        n_below[h] = (visible & (p < small_p)).sum(axis=1)", "        n_below[h] = (visible & (p > small_p)).sum(axis=1)"),
+    "summary_n_off_by_one": ("    n = (n_keys - w + 1 + np.arange(w)).astype(np.float64)", "    n = (n_keys - w + np.arange(w)).astype(np.float64)"),
+    "pivot_off_by_one": ("            return l\n    return L - 1", "            return l - 1\n    return L - 1"),
+    "pivot_fall_or_rise": ("        if fell and rose:", "        if fell or rose:"),
+    "pivot_absolute_drop": ("        fell = mean_entropy[l - 1] - mean_entropy[l] >= min_drop * mean_entropy[l - 1]",
+                            "        fell = mean_entropy[l - 1] - mean_entropy[l] >= min_drop"),
     "given_lse_sign": ("raw[h // G] += np.exp(logits - lse[h][:, None]).sum(axis=0)",
                        "raw[h // G] += np.exp(logits + lse[h][:, None]).sum(axis=0)"),
     "given_lse_no_mean": ("    return raw / G\n\n\ndef saliency_all_given_lse", "    return raw\n\n\ndef saliency_all_given_lse"),
