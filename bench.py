@@ -27,6 +27,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # sources of the kernels one kvsel_score call launches on the bf16 path
 SCORE_SOURCES = ("token_selection_amd/csrc/stream.hip+token_selection_amd/csrc/score.hip"
                  "+token_selection_amd/csrc/tile32.h")
+# ... and with the pivot statistics, also the per-layer summary kernel
+STATS_SOURCES = SCORE_SOURCES + "+token_selection_amd/csrc/pivot.hip"
 
 
 def recorded_traffic(kernel: str, sources: str):
@@ -100,9 +102,15 @@ def main() -> int:
     ap.add_argument("--lse-in", action="store_true",
                     help="score with the window rows' LSE handed in (kvsel_score_lse, one pass over K); the LSE "
                          "is computed once before timing, as prefill attention would have it")
+    ap.add_argument("--stats", action="store_true",
+                    help="score with the pivot statistics of every window row (kvsel_score_stats, then "
+                         "kvsel_layer_summary), as StructKV's pivot detection runs it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.stats and args.lse_in:
+        print("--stats and --lse-in are separate modes", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -155,11 +163,17 @@ def main() -> int:
         K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc, lse_out=lse_in)
         torch.cuda.synchronize()
 
+    small_p = 1.0 / N  # keys below the uniform share
+
     def step(evs=None):
         # evs: per-stage (start, end) events recorded on the launch stream
         if evs:
             evs["score"][0].record(stream)
-        if lse_in is None:
+        if args.stats:
+            _, ent, sp2, nb = K.kvsel_score_stats(q, k, scores, window=w, pool_kernel=wl.pool_kernel,
+                                                  small_p=small_p, workspace=ws, desc=desc)
+            K.kvsel_layer_summary(ent, sp2, nb, n_keys=N)
+        elif lse_in is None:
             K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
         else:
             K.kvsel_score_lse(q, k, lse_in, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
@@ -221,7 +235,8 @@ def main() -> int:
         "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "n_keys": wl.n_keys, "window": wl.window,
                    "pool": wl.pool_kernel, "kv_budget": wl.kv_budget,
-                   "lse": "computed (two passes)" if lse_in is None else "handed in (one pass)"},
+                   "lse": "computed (two passes)" if lse_in is None else "handed in (one pass)",
+                   "pivot_stats": bool(args.stats)},
         "hbm_gbs_whole_path": whole_gbs,
         "hbm_frac_whole_path": whole_gbs / HBM_PEAK_GBS,
         "stage_ms": stage_ms,
@@ -231,11 +246,14 @@ def main() -> int:
         # pass 2 and the pool), timed with HIP events on its launch stream;
         # algorithmic bytes = K read once + Q + final scores
         "roofline": {"bound": "hbm",
-                     "kernel": ("kvsel_score (stream_kernel pass 1 + merge + pass 2 + pool)" if lse_in is None
+                     "kernel": ("kvsel_score_stats (stream_kernel pass 1 + merge + pass 2 + count + pool + "
+                                "layer summary)" if args.stats else
+                                "kvsel_score (stream_kernel pass 1 + merge + pass 2 + pool)" if lse_in is None
                                 else "kvsel_score_lse (stream_kernel pass 2 + pool)"),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic("kvsel_score" if lse_in is None else "kvsel_score_lse",
-                                                 SCORE_SOURCES),
+                     "traffic": (recorded_traffic("kvsel_score_stats", STATS_SOURCES) if args.stats else
+                                 recorded_traffic("kvsel_score" if lse_in is None else "kvsel_score_lse",
+                                                  SCORE_SOURCES)),
                      "algorithmic_bytes": score_alg_bytes},
         "cpu_baseline": cpu,
         "wall_s_timed": wall,

@@ -128,6 +128,55 @@ kvsel_status_t kvsel_score_lse(const kvsel_score_desc_t* desc, const void* q_win
                                void* stream);
 
 /*
+ * Saliency scores plus the attention statistics of every window row that
+ * StructKV's dynamic pivot detection watches (StructKV section 2: attention
+ * entropy, sparsity and variance during the first pass, layer by layer).
+ *
+ * Same arguments and scores as kvsel_score, and:
+ * small_p  probability threshold of the count, 0 < small_p <= 1.
+ * entropy  device float[L][B][Hq][w]: -sum_j p_j ln p_j over the keys row i
+ *          sees (j <= N - w + i), p_j = exp(l_j - LSE), in nats.
+ * sum_p2   device float[L][B][Hq][w]: sum_j p_j^2 (the row's variance of
+ *          weights is sum_p2 / n - 1 / n^2 with n = N - w + i + 1).
+ * n_below  device int32[L][B][Hq][w]: the number of keys the row sees with
+ *          p_j < small_p (decided in fp32 on the logit: x < (log2(small_p) +
+ *          LSE2) / c; keys within rounding of the threshold may fall either way).
+ * Only the streaming path computes them: bf16, head_dim 64/128, G*w <= 256;
+ * other shapes return UNSUPPORTED. Both passes read every key.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+kvsel_status_t kvsel_score_stats(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
+                                 int32_t accumulate, float* lse_out, float small_p, float* entropy, float* sum_p2,
+                                 int32_t* n_below, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-layer means of the row statistics (StructKV section 2).
+ *
+ * entropy, sum_p2, n_below  device [n_layers][rows_per_layer] as written by
+ *          kvsel_score_stats, rows_per_layer = B*Hq*w (window index r % w).
+ * summary  device float[n_layers][3]: the means over the layer's rows of the
+ *          entropy, of the sparsity n_below / n and of the variance
+ *          sum_p2 / n - 1 / n^2, n = n_keys - window + 1 + (r % window).
+ * Errors: INVALID_ARG (rows_per_layer not a multiple of window, null
+ * pointers, sizes out of range), HIP.
+ */
+kvsel_status_t kvsel_layer_summary(int32_t n_layers, int32_t rows_per_layer, int32_t window, int64_t n_keys,
+                                   const float* entropy, const float* sum_p2, const int32_t* n_below, float* summary,
+                                   void* stream);
+
+/*
+ * StructKV's pivot layer (section 2, the phase transition where entropy falls
+ * and sparsity rises), on HOST arrays: the first layer l >= 1 with
+ *   mean_entropy[l-1] - mean_entropy[l] >= min_drop * mean_entropy[l-1]   and
+ *   mean_sparsity[l] - mean_sparsity[l-1] >= min_rise,
+ * compared in double; n_layers - 1 when there is none. Layers 0 .. *pivot are
+ * the ones whose scores are accumulated. Runs on the host only.
+ * Errors: INVALID_ARG (n_layers < 1, null pointers, non-finite thresholds).
+ */
+kvsel_status_t kvsel_pivot_layer(int32_t n_layers, const float* mean_entropy, const float* mean_sparsity,
+                                 float min_drop, float min_rise, int32_t* pivot);
+
+/*
  * Accumulate score vectors (StructKV section 1: a token's scores added up over
  * layers; FastKV section 2A: one token set per sequence for propagation).
  *

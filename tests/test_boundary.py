@@ -1,6 +1,7 @@
 """The C-ABI library: it loads, exports every function include/kvsel.h
 declares, its struct layout matches the binding, and every argument error is
-reported before any launch (these calls never reach the GPU). CPU only."""
+reported before any launch (these calls never reach the GPU). The host-only
+pivot rule is checked against the oracle here. CPU only."""
 
 import ctypes
 import os
@@ -8,7 +9,10 @@ import re
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
+
+import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvsel.h")
@@ -193,3 +197,69 @@ def test_score_lse_rejects(lib):
     assert lib.kvsel_score_lse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, need - 1, None) == 3
     bad = good_desc(head_dim=96)
     assert lib.kvsel_score_lse(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == 2
+
+
+def test_score_stats_rejects(lib):
+    d = good_desc()
+    need = lib.kvsel_score_workspace_bytes(ctypes.byref(d))
+    call = lambda desc, p, ent, sp2, nb: lib.kvsel_score_stats(ctypes.byref(desc), FAKE, FAKE, FAKE, 0, None, p,
+                                                               ent, sp2, nb, FAKE, need, None)
+    for p in (0.0, -1e-3, 1.5, float("nan"), float("inf")):
+        assert call(d, p, FAKE, FAKE, FAKE) == 1
+    assert call(d, 1e-3, None, FAKE, FAKE) == 1
+    assert call(d, 1e-3, FAKE, None, FAKE) == 1
+    assert call(d, 1e-3, FAKE, FAKE, None) == 1
+    # the statistics ride on the bf16 streaming passes only
+    f32 = good_desc(dtype=kvsel.KVSEL_DTYPE_F32, q_strides=[0, 0, 4 * 128, 128], k_strides=[0, 0, 1024 * 128, 128])
+    need32 = lib.kvsel_score_workspace_bytes(ctypes.byref(f32))
+    assert need32 > 0
+    assert lib.kvsel_score_stats(ctypes.byref(f32), FAKE, FAKE, FAKE, 0, None, 1e-3, FAKE, FAKE, FAKE, FAKE, need32,
+                                 None) == 2
+    assert lib.kvsel_score_stats(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, 1e-3, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                 None) == 3
+
+
+def test_layer_summary_rejects(lib):
+    ok = (2, 64, 16, 1000, FAKE, FAKE, FAKE, FAKE, None)
+    assert lib.kvsel_layer_summary(0, *ok[1:]) == 1
+    assert lib.kvsel_layer_summary(2, 60, *ok[2:]) == 1      # rows not a multiple of the window
+    assert lib.kvsel_layer_summary(2, 64, 16, 15, *ok[4:]) == 1  # fewer keys than the window
+    for i in range(4, 8):
+        bad = list(ok)
+        bad[i] = None
+        assert lib.kvsel_layer_summary(*bad) == 1
+
+
+def _pivot(lib, e, s, drop, rise):
+    n = len(e)
+    ea = (ctypes.c_float * max(n, 1))(*e)
+    sa = (ctypes.c_float * max(n, 1))(*s)
+    out = ctypes.c_int32(-7)
+    st = lib.kvsel_pivot_layer(n, ea, sa, drop, rise, ctypes.byref(out))
+    return st, out.value
+
+
+def test_pivot_layer_matches_oracle(lib):
+    """The host pivot rule against the oracle's, on the same float32 inputs:
+    hand-made transitions and seeded random walks."""
+    cases = [([10.0, 9.9, 9.8, 6.0, 5.9, 2.0], [0.10, 0.10, 0.12, 0.50, 0.52, 0.90], 0.1, 0.05),
+             ([10.0, 10.0, 5.0, 5.0], [0.0, 0.0, 0.5, 0.5], 0.1, 0.1),
+             ([7.0], [0.3], 0.1, 0.05)]
+    rng = np.random.default_rng(17)
+    for _ in range(300):
+        L = int(rng.integers(1, 40))
+        e = np.cumsum(-np.abs(rng.normal(0.0, 0.6, L))) + 12.0
+        sp = np.clip(np.cumsum(np.abs(rng.normal(0.0, 0.05, L))), 0.0, 1.0)
+        cases.append((e.astype(np.float32).tolist(), sp.astype(np.float32).tolist(),
+                      float(np.float32(rng.uniform(0.0, 0.2))), float(np.float32(rng.uniform(0.0, 0.1)))))
+    for e, sp, drop, rise in cases:
+        st, got = _pivot(lib, e, sp, drop, rise)
+        e32 = [float(np.float32(x)) for x in e]
+        s32 = [float(np.float32(x)) for x in sp]
+        assert st == 0 and got == oracle.pivot_layer(e32, s32, float(np.float32(drop)), float(np.float32(rise)))
+
+
+def test_pivot_layer_rejects(lib):
+    assert _pivot(lib, [], [], 0.1, 0.1)[0] == 1
+    assert _pivot(lib, [1.0], [0.0], float("nan"), 0.1)[0] == 1
+    assert lib.kvsel_pivot_layer(1, None, None, 0.1, 0.1, None) == 1

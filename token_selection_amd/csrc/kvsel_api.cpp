@@ -131,11 +131,19 @@ Path choose_path(const Plan& p) {
 
 kvsel_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
 
+// Pivot-statistics outputs of kvsel_score_stats.
+struct StatsOut {
+    float small_p;
+    float* entropy;
+    float* sum_p2;
+    int32_t* n_below;
+};
+
 // The scoring call. lse_in == null: both softmax passes (a1-a3). lse_in !=
 // null: the row LSEs are handed in and only the second pass runs.
 kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
                           int32_t accumulate, float* lse_out, const float* lse_in, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, const StatsOut* stats = nullptr) {
     const kvsel_status_t st = validate_desc(desc);
     if (st != KVSEL_OK) return st;
     if (!q_win || !k || !aligned16(q_win) || !aligned16(k)) return KVSEL_ERR_INVALID_ARG;
@@ -152,7 +160,8 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
     g.lse_in = lse_in;
     float* raw = nullptr;
     bool done = false;
-    Path path = choose_path(p);
+    if (stats && !p.stream.ok) return KVSEL_ERR_UNSUPPORTED;  // the statistics ride on the streaming passes
+    Path path = stats ? Path::Stream : choose_path(p);
     if (lse_in && path == Path::Resident) path = p.stream.ok ? Path::Stream : Path::General;
     if (path == Path::Stream) {
         kvsel::StreamArgs a;
@@ -175,9 +184,16 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         a.c = g.c;
         a.invG = g.invG;
         a.part = reinterpret_cast<float2*>(ws + p.stream.part_off);
+        a.part4 = reinterpret_cast<float4*>(ws + p.stream.part_off);
+        a.cnt_part = reinterpret_cast<uint32_t*>(ws + p.stream.cnt_off);
         a.lse2 = reinterpret_cast<float*>(ws + p.stream.lse2_off);
         a.raw = reinterpret_cast<float*>(ws + p.stream.raw_off);
-        if (lse_in) {
+        a.l2tau = stats ? log2f(stats->small_p) : 0.f;
+        if (stats) {
+            if (kvsel::launch_stream_stats(p.stream, a, lse_out, stats->entropy, stats->sum_p2, stats->n_below, hs) !=
+                hipSuccess)
+                return KVSEL_ERR_HIP;
+        } else if (lse_in) {
             if (kvsel::launch_lse_from_input(lse_in, a.lse2, g.S, p.stream.rp, g.R, g.w, g.B, g.Hq, g.Hkv, g.G, hs) !=
                     hipSuccess ||
                 kvsel::launch_stream_pass2(p.stream, a, hs) != hipSuccess)
@@ -275,6 +291,42 @@ kvsel_status_t kvsel_score_lse(const kvsel_score_desc_t* desc, const void* q_win
                                void* stream) {
     if (!lse_in) return KVSEL_ERR_INVALID_ARG;
     return score_impl(desc, q_win, k, scores, accumulate, nullptr, lse_in, workspace, workspace_bytes, stream);
+}
+
+kvsel_status_t kvsel_score_stats(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,
+                                 int32_t accumulate, float* lse_out, float small_p, float* entropy, float* sum_p2,
+                                 int32_t* n_below, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!entropy || !sum_p2 || !n_below) return KVSEL_ERR_INVALID_ARG;
+    if (!(small_p > 0.f && small_p <= 1.f)) return KVSEL_ERR_INVALID_ARG;  // also rejects NaN
+    const StatsOut so{small_p, entropy, sum_p2, n_below};
+    return score_impl(desc, q_win, k, scores, accumulate, lse_out, nullptr, workspace, workspace_bytes, stream, &so);
+}
+
+kvsel_status_t kvsel_layer_summary(int32_t n_layers, int32_t rows_per_layer, int32_t window, int64_t n_keys,
+                                   const float* entropy, const float* sum_p2, const int32_t* n_below, float* summary,
+                                   void* stream) {
+    if (n_layers < 1 || n_layers > 65535 || rows_per_layer < 1 || window < 1 || n_keys < window ||
+        n_keys >= kMaxKeys || rows_per_layer % window != 0)
+        return KVSEL_ERR_INVALID_ARG;
+    if (!entropy || !sum_p2 || !n_below || !summary) return KVSEL_ERR_INVALID_ARG;
+    return from_hip(kvsel::launch_layer_summary(n_layers, rows_per_layer, window, n_keys, entropy, sum_p2, n_below,
+                                                summary, static_cast<hipStream_t>(stream)));
+}
+
+kvsel_status_t kvsel_pivot_layer(int32_t n_layers, const float* mean_entropy, const float* mean_sparsity,
+                                 float min_drop, float min_rise, int32_t* pivot) {
+    if (n_layers < 1 || !mean_entropy || !mean_sparsity || !pivot) return KVSEL_ERR_INVALID_ARG;
+    if (!isfinite(min_drop) || !isfinite(min_rise)) return KVSEL_ERR_INVALID_ARG;
+    for (int32_t l = 1; l < n_layers; ++l) {
+        const double e0 = mean_entropy[l - 1], e1 = mean_entropy[l];
+        const double s0 = mean_sparsity[l - 1], s1 = mean_sparsity[l];
+        if (e0 - e1 >= (double)min_drop * e0 && s1 - s0 >= (double)min_rise) {
+            *pivot = l;
+            return KVSEL_OK;
+        }
+    }
+    *pivot = n_layers - 1;
+    return KVSEL_OK;
 }
 
 kvsel_status_t kvsel_accumulate(int32_t batch, int32_t n_heads, int64_t n, const float* src, float* dst,

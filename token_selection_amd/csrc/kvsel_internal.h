@@ -98,10 +98,13 @@ struct StreamArgs {
     int32_t N, Np, S;
     int32_t spp;      // segments per slab (set per pass)
     int32_t seg_len;  // keys per segment, a multiple of the 256-key chunk
-    int32_t n_range;  // keys the pass covers: N (pass 1) or Np (pass 2)
+    int32_t n_range;  // keys the pass covers: N (pass 1, and pass 2 with statistics) or Np (pass 2)
     int32_t n_seg;    // S * spp
     float c, invG;
+    float l2tau;   // statistics: log2 of the probability threshold of the count
     float2* part;  // [S][spp1][rp] per-segment (reference, sum) of every row, log2 domain
+    float4* part4; // statistics: [S][spp1][rp] (reference, sum, sum e*x, sum e^2), same place as part
+    uint32_t* cnt_part;  // statistics: [S][spp1][rp] per-segment counts of keys below the threshold
     float* lse2;   // [S][rp] row LSE2
     float* raw;    // [S][Np]
 };
@@ -110,16 +113,25 @@ struct StreamPlan {
     bool ok;
     int head_dim, rbn, rbn_cap, rp, n_wg;
     int spp1, seg_len1, spp2, seg_len2;
-    size_t part_off, lse2_off, raw_off;  // raw: [S][Np] floats at raw_off
+    size_t part_off, cnt_off, lse2_off, raw_off;  // raw: [S][Np] floats at raw_off
 };
 
 bool stream_plan(int dtype, int head_dim, int R, int64_t N, int64_t Np, int64_t S, int n_cu, StreamPlan& plan);
 hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, hipStream_t stream);
+// Both passes with the pivot statistics of every row: entropy, sum of p^2
+// ([L][B][Hq][w] floats) and the count of keys with p below the threshold
+// ([L][B][Hq][w] int32), besides the raw scores and the optional LSE.
+hipError_t launch_stream_stats(const StreamPlan& plan, StreamArgs a, float* lse_out, float* entropy, float* sum_p2,
+                               int32_t* n_below, hipStream_t stream);
 // Pass 2 alone, on row LSEs already in a.lse2.
 hipError_t launch_stream_pass2(const StreamPlan& plan, StreamArgs a, hipStream_t stream);
 
 hipError_t launch_accumulate(int32_t B, int32_t H, int64_t n, const float* src, float* dst, int mode,
                              hipStream_t stream);
+
+// Per-layer means [L][3] (entropy, sparsity, variance) of the row statistics.
+hipError_t launch_layer_summary(int32_t L, int32_t rows, int32_t w, int64_t N, const float* entropy,
+                                const float* sum_p2, const int32_t* n_below, float* summary, hipStream_t stream);
 
 size_t topk_workspace_bytes(int32_t rows, int64_t n_prefix);
 hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, int32_t n_sink,

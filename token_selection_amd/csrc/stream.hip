@@ -11,6 +11,12 @@
 //   stream_kernel<PASS=2>  per prefix key, sum over the rows of
 //                          exp2(c*x - LSE2), times 1/G -> raw scores.
 //
+// With ST (the pivot statistics of StructKV section 2) pass 1 also carries
+// each row's sum of e*x and e^2 (tile32.h), the merge turns them into the
+// row's entropy and sum of p^2, and pass 2 runs over all N keys and also counts
+// the keys each row sees with p below a threshold, from key-major tiles whose
+// lanes are rows.
+//
 // No work-group waits for another: every slab is cut into segments of whole
 // 256-key chunks, work-group g takes segments g, g + grid, ..., and while it
 // computes one chunk the loads of its next chunk are in flight into a second
@@ -20,6 +26,8 @@
 
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kvsel.h"
 #include "kvsel_internal.h"
@@ -88,19 +96,23 @@ __device__ __forceinline__ void load_chunk(Frag<D>& f, const StreamArgs& a, cons
     }
 }
 
-template <int D, int RBN>
+template <int D, int RBN, bool ST>
 struct Smem {
     static constexpr int RP = RBN * 32;
     static constexpr int QST = D + 8;  // LDS row stride in elements (16 bytes of padding)
+    static constexpr int SP = ST ? RP : 1;
+    using State = typename std::conditional<ST, float4, float2>::type;
     uint16_t q[RP * QST];
-    float2 st[kWaves][RP];  // pass 1: running (reference, sum) per wave and row
-    float lse[RP];          // pass 2: row LSE2 (+inf on padded rows)
+    State st[kWaves][RP];     // pass 1: running (reference, sum[, s, q]) per wave and row
+    float lse[RP];            // pass 2: row LSE2 (+inf on padded rows)
+    float thr[SP];            // pass 2 with ST: logit below which a key's p is under the threshold
+    uint32_t cnt[kWaves][SP]; // pass 2 with ST: per wave and row, keys counted so far
 };
 
 // Stage the query rows of a segment's slab (row r -> head g*G + r/w, window
 // index r%w; rows past R are zero) and reset or load the per-row state.
-template <int D, int RBN, int PASS>
-__device__ void stage(Smem<D, RBN>& sm, const StreamArgs& a, int seg, int tid) {
+template <int D, int RBN, int PASS, bool ST>
+__device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int tid) {
     constexpr int RP = RBN * 32;
     constexpr int QST = D + 8;
     constexpr int CPK = D / 8;  // 16-byte chunks per row
@@ -125,9 +137,19 @@ __device__ void stage(Smem<D, RBN>& sm, const StreamArgs& a, int seg, int tid) {
         }
     }
     if (PASS == 1) {
-        for (int i = tid; i < kWaves * RP; i += 256) (&sm.st[0][0])[i] = make_float2(kNegBig, 0.f);
+        if constexpr (ST) {
+            for (int i = tid; i < kWaves * RP; i += 256) (&sm.st[0][0])[i] = make_float4(kNegBig, 0.f, 0.f, 0.f);
+        } else {
+            for (int i = tid; i < kWaves * RP; i += 256) (&sm.st[0][0])[i] = make_float2(kNegBig, 0.f);
+        }
     } else {
-        for (int row = tid; row < RP; row += 256) sm.lse[row] = row < a.R ? a.lse2[(int64_t)slab * RP + row] : INFINITY;
+        for (int row = tid; row < RP; row += 256) {
+            const float l2 = row < a.R ? a.lse2[(int64_t)slab * RP + row] : INFINITY;
+            sm.lse[row] = l2;
+            if constexpr (ST) sm.thr[row] = (a.l2tau + l2) / a.c;  // c*x - LSE2 < log2(tau)  <=>  x < thr
+        }
+        if constexpr (ST)
+            for (int i = tid; i < kWaves * RP; i += 256) (&sm.cnt[0][0])[i] = 0u;
     }
 #pragma unroll
     for (int u = 0; u < QPER; ++u) {
@@ -141,8 +163,8 @@ __device__ void stage(Smem<D, RBN>& sm, const StreamArgs& a, int seg, int tid) {
 
 // Pass 1 on one chunk: merge this wave's (reference, sum) of every row into
 // its running state.
-template <int D, int RBN>
-__device__ __forceinline__ void pass1_chunk(Smem<D, RBN>& sm, const StreamArgs& a, const Frag<D>& f,
+template <int D, int RBN, bool ST>
+__device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamArgs& a, const Frag<D>& f,
                                             const Cursor& c, int wave, int col, int hf) {
     constexpr int KS = D / 16;
     constexpr int QST = D + 8;
@@ -157,31 +179,51 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN>& sm, const StreamArgs& 
             qf[ks] = *reinterpret_cast<const bf16x8*>(sm.q + (rb * 32 + col) * QST + ks * 16 + hf * 8);
         // lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
         float m, z;
-        if (edge) {
-            const int row = rb * 32 + col;
-            const int lim = row < a.R ? a.Np + row % a.w : -1;
-            z = pass1_max<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m);
+        if constexpr (ST) {
+            Moments mo;
+            if (edge) {
+                const int row = rb * 32 + col;
+                const int lim = row < a.R ? a.Np + row % a.w : -1;
+                z = pass1_max_st<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m, mo);
+            } else {
+                z = pass1_fast_st<D, kKB>(f.v, qf, a.c, m, mo);
+                if (__any(!(z < kOverflowSt))) z = pass1_max_st<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m, mo);
+            }
+            merge_st(m, z, mo, __shfl_xor(m, 32), __shfl_xor(z, 32),
+                     Moments{__shfl_xor(mo.s, 32), __shfl_xor(mo.q, 32)});
+            if (hf == 0) {
+                float4 st = sm.st[wave][rb * 32 + col];
+                Moments sa{st.z, st.w};
+                merge_st(st.x, st.y, sa, m, z, mo);
+                sm.st[wave][rb * 32 + col] = make_float4(st.x, st.y, sa.s, sa.q);
+            }
         } else {
-            z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
-            if (__any(!(z < kOverflow))) z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
-        }
-        merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));  // the two lane halves: same row, other keys
-        if (hf == 0) {
-            float2 st = sm.st[wave][rb * 32 + col];
-            merge(st.x, st.y, m, z);
-            sm.st[wave][rb * 32 + col] = st;
+            if (edge) {
+                const int row = rb * 32 + col;
+                const int lim = row < a.R ? a.Np + row % a.w : -1;
+                z = pass1_max<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m);
+            } else {
+                z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
+                if (__any(!(z < kOverflow))) z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
+            }
+            merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));  // the two lane halves: same row, other keys
+            if (hf == 0) {
+                float2 st = sm.st[wave][rb * 32 + col];
+                merge(st.x, st.y, m, z);
+                sm.st[wave][rb * 32 + col] = st;
+            }
         }
     }
 }
 
 // Pass 2 on one chunk: raw score of each of this wave's prefix keys.
-template <int D, int RBN>
-__device__ __forceinline__ void pass2_chunk(Smem<D, RBN>& sm, const StreamArgs& a, const Frag<D>& f,
+template <int D, int RBN, bool ST>
+__device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamArgs& a, const Frag<D>& f,
                                             const Cursor& c, int wave, int col, int hf) {
     constexpr int KS = D / 16;
     constexpr int QST = D + 8;
     const int kbase = c.first + wave * kWaveKeys;
-    if (kbase >= a.Np) return;  // no prefix keys in this wave's range
+    if (kbase >= a.n_range) return;  // no keys of this pass in this wave's range
     float cs0 = 0.f, cs1 = 0.f;
 #pragma unroll 1
     for (int rb = 0; rb < a.rbn; ++rb) {
@@ -216,6 +258,23 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN>& sm, const StreamArgs& 
             s1 += fexp2(x1[v + 1] * a.c - lr[v + 1]);
         }
         cs1 += s0 + s1;
+        if constexpr (ST) {
+            // key-major tiles: lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
+            const int row = rb * 32 + col;
+            const float thr = sm.thr[row];
+            const bool edge = kbase + kWaveKeys > a.Np;  // reaches the window (causal mask) or the end
+            const int lim = row < a.R ? a.Np + row % a.w : -1;
+            uint32_t n = 0;
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb) {
+                const f32x16 y = logits<KS>(f.v[kb], qf);
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    n += (y[v] < thr && (!edge || kbase + kb * 32 + tile_row(v, hf) <= lim)) ? 1u : 0u;
+            }
+            n += __shfl_xor(n, 32);
+            if (hf == 0) sm.cnt[wave][row] += n;
+        }
     }
     const int slab = c.seg / a.spp;
     const float v0 = cs0 + __shfl_xor(cs0, 32);
@@ -227,44 +286,69 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN>& sm, const StreamArgs& 
 }
 
 // Pass 1, end of a segment: merge the waves' states and publish the partials.
-template <int D, int RBN>
-__device__ __forceinline__ void pass1_finish(Smem<D, RBN>& sm, const StreamArgs& a, int seg, int tid) {
+template <int D, int RBN, bool ST>
+__device__ __forceinline__ void pass1_finish(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int tid) {
     constexpr int RP = RBN * 32;
     __syncthreads();
     for (int row = tid; row < RP; row += 256) {
-        float2 acc = sm.st[0][row];
+        if constexpr (ST) {
+            float4 acc = sm.st[0][row];
+            Moments ma{acc.z, acc.w};
 #pragma unroll
-        for (int w2 = 1; w2 < kWaves; ++w2) merge(acc.x, acc.y, sm.st[w2][row].x, sm.st[w2][row].y);
-        a.part[(int64_t)seg * RP + row] = acc;
+            for (int w2 = 1; w2 < kWaves; ++w2) {
+                const float4 o = sm.st[w2][row];
+                merge_st(acc.x, acc.y, ma, o.x, o.y, Moments{o.z, o.w});
+            }
+            a.part4[(int64_t)seg * RP + row] = make_float4(acc.x, acc.y, ma.s, ma.q);
+        } else {
+            float2 acc = sm.st[0][row];
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves; ++w2) merge(acc.x, acc.y, sm.st[w2][row].x, sm.st[w2][row].y);
+            a.part[(int64_t)seg * RP + row] = acc;
+        }
+    }
+}
+
+// Pass 2 with ST, end of a segment: the waves' counts of every row.
+template <int D, int RBN>
+__device__ __forceinline__ void pass2_finish(Smem<D, RBN, true>& sm, const StreamArgs& a, int seg, int tid) {
+    constexpr int RP = RBN * 32;
+    __syncthreads();
+    for (int row = tid; row < RP; row += 256) {
+        uint32_t n = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) n += sm.cnt[w2][row];
+        a.cnt_part[(int64_t)seg * RP + row] = n;
     }
 }
 
 // One chunk with its keys in `f` while the next chunk's keys load into `g`.
 // Returns false once the work-group's sequence ends.
-template <int D, int RBN, int PASS>
-__device__ __forceinline__ bool step(Smem<D, RBN>& sm, const StreamArgs& a, Cursor& cur, Frag<D>& f, Frag<D>& g,
-                                     int tid, int wave, int col, int hf) {
+template <int D, int RBN, int PASS, bool ST>
+__device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, const StreamArgs& a, Cursor& cur, Frag<D>& f,
+                                     Frag<D>& g, int tid, int wave, int col, int hf) {
     const Cursor nx = advance(a, cur);
     // Issued on every step (the last one re-reads the current chunk): with a
     // fixed number of loads in flight the wait for `f` leaves `g`'s in flight.
     load_chunk<D>(g, a, nx.seg >= 0 ? nx : cur, wave, col, hf);
     if (PASS == 1)
-        pass1_chunk<D, RBN>(sm, a, f, cur, wave, col, hf);
+        pass1_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf);
     else
-        pass2_chunk<D, RBN>(sm, a, f, cur, wave, col, hf);
+        pass2_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf);
     if (nx.seg != cur.seg) {
-        if (PASS == 1) pass1_finish<D, RBN>(sm, a, cur.seg, tid);
+        if (PASS == 1) pass1_finish<D, RBN, ST>(sm, a, cur.seg, tid);
+        if constexpr (ST && PASS == 2) pass2_finish<D, RBN>(sm, a, cur.seg, tid);
         if (nx.seg < 0) return false;
-        stage<D, RBN, PASS>(sm, a, nx.seg, tid);
+        stage<D, RBN, PASS, ST>(sm, a, nx.seg, tid);
     }
     cur = nx;
     return true;
 }
 
-template <int D, int RBN, int PASS>
+template <int D, int RBN, int PASS, bool ST>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 stream_kernel(StreamArgs a) {
-    __shared__ __attribute__((aligned(16))) Smem<D, RBN> sm;
+    __shared__ __attribute__((aligned(16))) Smem<D, RBN, ST> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -282,11 +366,11 @@ stream_kernel(StreamArgs a) {
     if (cur.seg < 0) return;
     Frag<D> fa, fb;
     load_chunk<D>(fa, a, cur, wave, col, hf);
-    stage<D, RBN, PASS>(sm, a, cur.seg, tid);
+    stage<D, RBN, PASS, ST>(sm, a, cur.seg, tid);
 
     for (;;) {
-        if (!step<D, RBN, PASS>(sm, a, cur, fa, fb, tid, wave, col, hf)) break;
-        if (!step<D, RBN, PASS>(sm, a, cur, fb, fa, tid, wave, col, hf)) break;
+        if (!step<D, RBN, PASS, ST>(sm, a, cur, fa, fb, tid, wave, col, hf)) break;
+        if (!step<D, RBN, PASS, ST>(sm, a, cur, fb, fa, tid, wave, col, hf)) break;
     }
 }
 
@@ -314,22 +398,68 @@ __global__ void stream_merge_kernel(const float2* part, int spp, int rp, int R, 
     }
 }
 
+// Output index of slab row `row`: (layer, b, head g*G + row / w, row % w).
+__device__ __forceinline__ int64_t row_out(int slab, int row, int w, int B, int Hq, int Hkv, int G) {
+    const int g = slab % Hkv;
+    const int b = (slab / Hkv) % B;
+    const int l = slab / (Hkv * B);
+    return (((int64_t)l * B + b) * Hq + g * G + row / w) * w + row % w;
+}
+
+// ST merge: row LSE2 as above, plus the row's entropy
+// -sum p ln p = ln2 * (LSE2 - c * sum p*x) and sum p^2 = q / z^2.
+__global__ void stream_merge_st_kernel(const float4* part, int spp, int rp, int R, int w, int B, int Hq, int Hkv,
+                                       int G, float c, float* lse2, float* lse_out, float* entropy,
+                                       float* sum_p2) {
+    const int slab = blockIdx.x;
+    for (int row = threadIdx.x; row < R; row += blockDim.x) {
+        float M = kNegBig, Z = 0.f;
+        Moments mo{0.f, 0.f};
+        for (int p = 0; p < spp; ++p) {
+            const float4 v = part[((int64_t)slab * spp + p) * rp + row];
+            merge_st(M, Z, mo, v.x, v.y, Moments{v.z, v.w});
+        }
+        const float l2 = M + log2f(Z);
+        lse2[(int64_t)slab * rp + row] = l2;
+        const int64_t o = row_out(slab, row, w, B, Hq, Hkv, G);
+        constexpr float kLn2 = 0.69314718055994530942f;
+        if (lse_out) lse_out[o] = l2 * kLn2;
+        entropy[o] = kLn2 * (l2 - c * (mo.s / Z));
+        sum_p2[o] = mo.q / (Z * Z);
+    }
+}
+
+// ST: every row's count of keys below the threshold, summed over segments.
+__global__ void stream_count_kernel(const uint32_t* cnt_part, int spp, int rp, int R, int w, int B, int Hq, int Hkv,
+                                    int G, int32_t* n_below) {
+    const int slab = blockIdx.x;
+    for (int row = threadIdx.x; row < R; row += blockDim.x) {
+        uint32_t n = 0;
+        for (int p = 0; p < spp; ++p) n += cnt_part[((int64_t)slab * spp + p) * rp + row];
+        n_below[row_out(slab, row, w, B, Hq, Hkv, G)] = (int32_t)n;
+    }
+}
+
 typedef void (*stream_fn)(StreamArgs);
 
-template <int D, int PASS>
+template <int D, int PASS, bool ST>
 stream_fn pick_rbn(int RBN) {
     switch (RBN) {
-        case 1: return stream_kernel<D, 1, PASS>;
-        case 2: return stream_kernel<D, 2, PASS>;
-        case 4: return stream_kernel<D, 4, PASS>;
-        case 8: return stream_kernel<D, 8, PASS>;
+        case 1: return stream_kernel<D, 1, PASS, ST>;
+        case 2: return stream_kernel<D, 2, PASS, ST>;
+        case 4: return stream_kernel<D, 4, PASS, ST>;
+        case 8: return stream_kernel<D, 8, PASS, ST>;
         default: return nullptr;
     }
 }
 
-stream_fn pick(int D, int RBN, int PASS) {
-    if (D == 128) return PASS == 1 ? pick_rbn<128, 1>(RBN) : pick_rbn<128, 2>(RBN);
-    return PASS == 1 ? pick_rbn<64, 1>(RBN) : pick_rbn<64, 2>(RBN);
+stream_fn pick(int D, int RBN, int PASS, bool ST = false) {
+    if (ST) {
+        if (D == 128) return PASS == 1 ? pick_rbn<128, 1, true>(RBN) : pick_rbn<128, 2, true>(RBN);
+        return PASS == 1 ? pick_rbn<64, 1, true>(RBN) : pick_rbn<64, 2, true>(RBN);
+    }
+    if (D == 128) return PASS == 1 ? pick_rbn<128, 1, false>(RBN) : pick_rbn<128, 2, false>(RBN);
+    return PASS == 1 ? pick_rbn<64, 1, false>(RBN) : pick_rbn<64, 2, false>(RBN);
 }
 
 int pow2_at_least(int x) {
@@ -366,8 +496,9 @@ bool stream_plan(int dtype, int head_dim, int R, int64_t N, int64_t Np, int64_t 
     plan.n_wg = 2 * n_cu;
     segments(N, S, plan.n_wg, plan.spp1, plan.seg_len1);
     segments(Np > 0 ? Np : 1, S, plan.n_wg, plan.spp2, plan.seg_len2);
-    plan.part_off = 0;
-    plan.lse2_off = align256((size_t)S * plan.spp1 * plan.rp * sizeof(float2));
+    plan.part_off = 0;  // float2 partials, or float4 with the pivot statistics
+    plan.cnt_off = align256((size_t)S * plan.spp1 * plan.rp * sizeof(float4));
+    plan.lse2_off = align256(plan.cnt_off + (size_t)S * plan.spp1 * plan.rp * sizeof(uint32_t));
     plan.raw_off = align256(plan.lse2_off + (size_t)S * plan.rp * sizeof(float));
     plan.ok = pick(head_dim, plan.rbn_cap, 1) != nullptr;
     return plan.ok;
@@ -386,6 +517,26 @@ hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, h
     hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.part, plan.spp1, plan.rp, a.R,
                        a.w, a.B, a.Hq, a.Hkv, a.G, a.lse2, lse_out);
     return launch_stream_pass2(plan, a, st);
+}
+
+hipError_t launch_stream_stats(const StreamPlan& plan, StreamArgs a, float* lse_out, float* entropy, float* sum_p2,
+                               int32_t* n_below, hipStream_t st) {
+    stream_fn f1 = pick(plan.head_dim, plan.rbn_cap, 1, true);
+    stream_fn f2 = pick(plan.head_dim, plan.rbn_cap, 2, true);
+    if (!f1 || !f2) return hipErrorInvalidValue;
+    // both passes over every key: pass 2 also counts the window keys each row sees
+    a.spp = plan.spp1;
+    a.seg_len = plan.seg_len1;
+    a.n_range = a.N;
+    a.n_seg = a.S * plan.spp1;
+    const unsigned grid = (unsigned)(a.n_seg < plan.n_wg ? a.n_seg : plan.n_wg);
+    hipLaunchKernelGGL(f1, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(stream_merge_st_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.part4, plan.spp1, plan.rp,
+                       a.R, a.w, a.B, a.Hq, a.Hkv, a.G, a.c, a.lse2, lse_out, entropy, sum_p2);
+    hipLaunchKernelGGL(f2, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(stream_count_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.cnt_part, plan.spp1, plan.rp,
+                       a.R, a.w, a.B, a.Hq, a.Hkv, a.G, n_below);
+    return hipGetLastError();
 }
 
 hipError_t launch_stream_pass2(const StreamPlan& plan, StreamArgs a, hipStream_t st) {

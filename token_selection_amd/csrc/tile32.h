@@ -110,5 +110,82 @@ __device__ __forceinline__ float pass1_max(const bf16x8 (&kf)[KB][D / 16], const
     return (zs[0] + zs[1]) + (zs[2] + zs[3]);
 }
 
+// Pivot statistics ride on pass 1: next to the sum z of exp2(c*x - ref) a row
+// carries s = sum of exp2(c*x - ref) * x and q = sum of exp2(c*x - ref)^2 on the
+// same reference, so that sum p*x = s / z and sum p^2 = q / z^2 once the
+// reference is final. With them the fast path needs a tighter overflow bound:
+// z < 2^40 keeps q <= z^2 finite.
+constexpr float kOverflowSt = 0x1p40f;
+
+struct Moments {
+    float s, q;
+};
+
+__device__ __forceinline__ void merge_st(float& m, float& z, Moments& a, float mo, float zo, Moments b) {
+    const float mn = fmaxf(m, mo);
+    const float f = fexp2(m - mn);
+    const float g = fexp2(mo - mn);
+    z = z * f + zo * g;
+    a.s = a.s * f + b.s * g;
+    a.q = a.q * (f * f) + b.q * (g * g);
+    m = mn;
+}
+
+template <int D, int KB>
+__device__ __forceinline__ float pass1_fast_st(const bf16x8 (&kf)[KB][D / 16], const bf16x8 (&qf)[D / 16], float c,
+                                               float& ref, Moments& mo) {
+    constexpr int KS = D / 16;
+    f32x16 cur = logits<KS>(kf[0], qf);
+    ref = cur[0] * c;
+    float zs[2] = {0.f, 0.f}, ss[2] = {0.f, 0.f}, qs[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        f32x16 nxt;
+        if (kb + 1 < KB) nxt = logits<KS>(kf[kb + 1], qf);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float e = fexp2(cur[v] * c - ref);
+            zs[v & 1] += e;
+            ss[v & 1] += e * cur[v];
+            qs[v & 1] += e * e;
+        }
+        if (kb + 1 < KB) cur = nxt;
+    }
+    mo.s = ss[0] + ss[1];
+    mo.q = qs[0] + qs[1];
+    return zs[0] + zs[1];
+}
+
+template <int D, int KB, bool MASK>
+__device__ __forceinline__ float pass1_max_st(const bf16x8 (&kf)[KB][D / 16], const bf16x8 (&qf)[D / 16], float c,
+                                              int kfirst, int hf, int lim, float& ref, Moments& mo) {
+    constexpr int KS = D / 16;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const f32x16 acc = logits<KS>(kf[kb], qf);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            if (!MASK || kfirst + kb * 32 + tile_row(v, hf) <= lim) mx = fmaxf(mx, acc[v]);
+    }
+    ref = fmaxf(kNegBig, mx * c);
+    float zs[2] = {0.f, 0.f}, ss[2] = {0.f, 0.f}, qs[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const f32x16 acc = logits<KS>(kf[kb], qf);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            if (!MASK || kfirst + kb * 32 + tile_row(v, hf) <= lim) {
+                const float e = fexp2(acc[v] * c - ref);
+                zs[v & 1] += e;
+                ss[v & 1] += e * acc[v];
+                qs[v & 1] += e * e;
+            }
+    }
+    mo.s = ss[0] + ss[1];
+    mo.q = qs[0] + qs[1];
+    return zs[0] + zs[1];
+}
+
 }  // namespace tile
 }  // namespace kvsel

@@ -35,6 +35,9 @@ EXPORTED = (
     "kvsel_score_workspace_bytes",
     "kvsel_score",
     "kvsel_score_lse",
+    "kvsel_score_stats",
+    "kvsel_layer_summary",
+    "kvsel_pivot_layer",
     "kvsel_accumulate",
     "kvsel_topk_workspace_bytes",
     "kvsel_topk",
@@ -90,6 +93,14 @@ def load_library() -> ctypes.CDLL:
     lib.kvsel_score.argtypes = [ctypes.POINTER(ScoreDesc), vp, vp, vp, i32, vp, vp, sz, vp]
     lib.kvsel_score.restype = i32
     lib.kvsel_score_lse.argtypes = [ctypes.POINTER(ScoreDesc), vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.kvsel_score_stats.argtypes = [ctypes.POINTER(ScoreDesc), vp, vp, vp, i32, vp, ctypes.c_float, vp, vp, vp, vp,
+                                      sz, vp]
+    lib.kvsel_score_stats.restype = i32
+    lib.kvsel_layer_summary.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, vp]
+    lib.kvsel_layer_summary.restype = i32
+    lib.kvsel_pivot_layer.argtypes = [i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                      ctypes.c_float, ctypes.c_float, ctypes.POINTER(i32)]
+    lib.kvsel_pivot_layer.restype = i32
     lib.kvsel_score_lse.restype = i32
     lib.kvsel_accumulate.argtypes = [i32, i32, i64, vp, vp, i32, vp]
     lib.kvsel_accumulate.restype = i32
@@ -238,6 +249,67 @@ def kvsel_score_lse(q_win: torch.Tensor, k: torch.Tensor, lse_in: torch.Tensor,
                              1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(dev, stream))
     _check(st, "kvsel_score_lse")
     return scores
+
+
+def kvsel_score_stats(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Tensor] = None, *, window: int,
+                      small_p: float, pool_kernel: int = 7, accumulate: bool = False, lse_out=None,
+                      softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None,
+                      desc: Optional[ScoreDesc] = None, pool_type: int = 0):
+    """As kvsel_score, also returning every window row's attention entropy,
+    sum of p^2 and count of keys with p < small_p ([L, B, Hq, w] each):
+    (scores, entropy, sum_p2, n_below)."""
+    lib = load_library()
+    if desc is None:
+        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type)
+    L, B, Hq, Hkv, N, w = desc.n_layers, desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.n_keys, desc.window
+    dev = k.device
+    if scores is None:
+        scores = torch.empty((B, Hkv, N - w), dtype=torch.float32, device=dev)
+    if scores.dtype != torch.float32 or not scores.is_contiguous() or tuple(scores.shape) != (B, Hkv, N - w):
+        raise ValueError("scores must be a contiguous float32 [B, Hkv, N - w] tensor")
+    if lse_out is not None and (lse_out.dtype != torch.float32 or not lse_out.is_contiguous() or
+                                lse_out.numel() != L * B * Hq * w):
+        raise ValueError("lse_out must be a contiguous float32 [L, B, Hq, w] tensor")
+    entropy = torch.empty((L, B, Hq, w), dtype=torch.float32, device=dev)
+    sum_p2 = torch.empty_like(entropy)
+    n_below = torch.empty((L, B, Hq, w), dtype=torch.int32, device=dev)
+    need = int(lib.kvsel_score_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kvsel_score_stats(ctypes.byref(desc), _ptr(q_win), _ptr(k), _ptr(scores), 1 if accumulate else 0,
+                               _ptr(lse_out), float(small_p), _ptr(entropy), _ptr(sum_p2), _ptr(n_below),
+                               _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    _check(st, "kvsel_score_stats")
+    return scores, entropy, sum_p2, n_below
+
+
+def kvsel_layer_summary(entropy: torch.Tensor, sum_p2: torch.Tensor, n_below: torch.Tensor, *, n_keys: int,
+                        stream=None) -> torch.Tensor:
+    """Per-layer means [L, 3] (entropy, sparsity, variance) of kvsel_score_stats'
+    row statistics [L, B, Hq, w]."""
+    lib = load_library()
+    for t, dt in ((entropy, torch.float32), (sum_p2, torch.float32), (n_below, torch.int32)):
+        if t.dim() != 4 or t.dtype != dt or not t.is_contiguous() or t.shape != entropy.shape:
+            raise ValueError("statistics must be contiguous [L, B, Hq, w] tensors (float32, float32, int32)")
+    L, B, Hq, w = entropy.shape
+    out = torch.empty((L, 3), dtype=torch.float32, device=entropy.device)
+    _check(lib.kvsel_layer_summary(L, B * Hq * w, w, n_keys, _ptr(entropy), _ptr(sum_p2), _ptr(n_below), _ptr(out),
+                                   _stream(entropy.device, stream)), "kvsel_layer_summary")
+    return out
+
+
+def kvsel_pivot_layer(mean_entropy, mean_sparsity, *, min_drop: float, min_rise: float) -> int:
+    """StructKV's pivot layer from per-layer means (host sequences of floats)."""
+    lib = load_library()
+    e = [float(x) for x in mean_entropy]
+    sp = [float(x) for x in mean_sparsity]
+    if len(e) != len(sp):
+        raise ValueError("one entropy and one sparsity value per layer")
+    ea = (ctypes.c_float * max(len(e), 1))(*e)
+    sa = (ctypes.c_float * max(len(sp), 1))(*sp)
+    out = ctypes.c_int32(-1)
+    _check(lib.kvsel_pivot_layer(len(e), ea, sa, min_drop, min_rise, ctypes.byref(out)), "kvsel_pivot_layer")
+    return int(out.value)
 
 
 # ---------------------------------------------------------------------------

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, replace
-from typing import Optional
+from typing import Optional, Tuple
 
 
 def budget_from_rate(rate: float, n_keys: int, window: int) -> int:
@@ -53,6 +53,7 @@ class Workload:
     hidden_dim: Optional[int] = None   # hidden-state width gathered by the token set
     query_model: str = "gauss"         # "gauss" | "zero"
     k_mult: float = 1.0                # extra multiplier on every key (stability cases)
+    layer_k_mult: Optional[Tuple[float, ...]] = None  # per-layer key multiplier (sharper attention where larger)
 
     # derived sizes -------------------------------------------------------
     @property

@@ -12,6 +12,9 @@ Recipe (everything drawn from ``numpy.random.default_rng`` seeded with a
   position (``"const"``, used for exact-tie cases). Keys are drawn in blocks of
   ``KEY_BLOCK`` positions, each block with its own seed (AR(1) carries its
   state across blocks).
+* ``k_mult`` scales every key; ``layer_k_mult[l]`` scales the keys of layer l
+  (larger keys spread the logits, so that layer's attention is sharper: lower
+  entropy, more near-zero weights).
 * RoPE (rotate-half convention, theta_i = base^(-2i/d)) is applied in fp64 to
   Q and K at their positions when the workload names a base.
 * Hubs: ``n_hubs`` positions drawn once per workload from [1, N - w), shared
@@ -149,6 +152,8 @@ def _key_block(wl: Workload, seed: int, layer: int, b: int, g: int, blk: int,
         k = rng.standard_normal((n, d))
     if wl.k_mult != 1.0:
         k *= wl.k_mult
+    if wl.layer_k_mult is not None:
+        k *= wl.layer_k_mult[layer]
     if wl.rope_base is not None:
         k = _rope(k, np.arange(j0, j1), wl.rope_base)
     if hubs_on and hubs.size:
