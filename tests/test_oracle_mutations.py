@@ -7,9 +7,12 @@ import types
 
 import pytest
 
+import centroid_checks
 import oracle_checks
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "kvsel_oracle.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "kvsel_oracle.py")
+CENTROID_SRC = os.path.join(ORACLE_DIR, "centroid_oracle.py")
 
 MUTATIONS = {
     "no_causal_mask": ("future = j > (N - w + i)", "future = j > N"),
@@ -60,8 +63,27 @@ MUTATIONS = {
 }
 
 
-def _mutant(old, new):
-    text = open(SRC).read()
+CENTROID_MUTATIONS = {
+    "csm_partition_swapped": ("    a_pos = [p for (s, e) in chunks for p in range(s, e, 2)]",
+                              "    a_pos = [p for (s, e) in chunks for p in range(s + 1, e, 2)]"),
+    "csm_chunks_from_zero": ("    chunks = [(s, min(s + chunk, hi)) for s in range(lo, hi, chunk)]",
+                             "    chunks = [(max(s, lo), min(s + chunk, hi)) for s in range(0, hi, chunk)]"),
+    "csm_tie_to_higher_b": ("                if c > best:", "                if c >= best:"),
+    "csm_dot_not_cosine": ("    return float(np.dot(a, b)) / (na * nb)", "    return float(np.dot(a, b))"),
+    "csm_select_ties_high": ("    order = np.lexsort((np.arange(score.shape[0]), -score))",
+                             "    order = np.lexsort((-np.arange(score.shape[0]), -score))"),
+    "csm_unweighted_mean": ("    wk = k * degree[:, None]", "    wk = k * 1.0"),
+    "csm_degree_not_summed": ("        deg[b] += degree[a]", "        deg[b] += 1"),
+    "csm_recent_in_middle": ("    lo, hi = n_sink, n - n_recent", "    lo, hi = n_sink, n"),
+    "attn_no_log_degree": ("            logit = logit + np.log(np.asarray(degree[g], dtype=np.float64))", "            pass"),
+    "attn_log_sign": ("            logit = logit + np.log(np.asarray(degree[g], dtype=np.float64))",
+                      "            logit = logit - np.log(np.asarray(degree[g], dtype=np.float64))"),
+    "attn_wrong_group": ("        g = h // G\n        logit", "        g = h % Hkv\n        logit"),
+}
+
+
+def _mutant(old, new, src=SRC):
+    text = open(src).read()
     assert text.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
     mod = types.ModuleType("kvsel_oracle_mutant")
     exec(compile(text.replace(old, new), "kvsel_oracle_mutant", "exec"), mod.__dict__)
@@ -76,5 +98,17 @@ def test_pins_catch_planted_mistake(name):
         try:
             check(mod)
         except Exception as e:  # AssertionError, or the mutant blowing up
+            failed.append(check.__name__)
+    assert failed, f"no pin caught mutation {name}"
+
+
+@pytest.mark.parametrize("name", sorted(CENTROID_MUTATIONS))
+def test_centroid_pins_catch_planted_mistake(name):
+    mod = _mutant(*CENTROID_MUTATIONS[name], src=CENTROID_SRC)
+    failed = []
+    for check in centroid_checks.CENTROID_CHECKS:
+        try:
+            check(mod)
+        except Exception:
             failed.append(check.__name__)
     assert failed, f"no pin caught mutation {name}"

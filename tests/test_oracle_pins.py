@@ -3,10 +3,12 @@ forms, library routines, invariants). CPU only."""
 
 import pytest
 
+import centroid_checks
 import oracle
 import oracle_checks
 
 
-@pytest.mark.parametrize("check", oracle_checks.ALL_CHECKS, ids=lambda c: c.__name__)
+@pytest.mark.parametrize("check", oracle_checks.ALL_CHECKS + centroid_checks.CENTROID_CHECKS,
+                         ids=lambda c: c.__name__)
 def test_oracle_pin(check):
     check(oracle)
