@@ -105,6 +105,12 @@ def main() -> int:
     ap.add_argument("--stats", action="store_true",
                     help="score with the pivot statistics of every window row (kvsel_score_stats, then "
                          "kvsel_layer_summary), as StructKV's pivot detection runs it")
+    ap.add_argument("--decode", action="store_true",
+                    help="time one decode step of attention over the 16-layer 128K workload's compacted cache "
+                         "(kvsel_decode_attention) instead of the selection path")
+    ap.add_argument("--csm", action="store_true",
+                    help="time one CentroidKV chunked-soft-matching round (kvsel_csm) on the batched 8 x 32K "
+                         "workload instead of the selection path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -130,6 +136,9 @@ def main() -> int:
 
     from token_selection_amd import kvsel as K
     from workloads import get_workload, make_inputs
+
+    if args.decode or args.csm:
+        return bench_extra(args, K, get_workload, make_inputs)
 
     wl = get_workload(args.workload)
     dev = torch.device("cuda:0")
@@ -258,6 +267,124 @@ def main() -> int:
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
     }
+    print(json.dumps(line))
+    return 0
+
+
+def timed(fn, stream, steps, warmup):
+    """Warm-up calls, then `steps` calls between two HIP events on the launch
+    stream: mean ms per call."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def bench_extra(args, K, get_workload, make_inputs) -> int:
+    """The two steps beside the selection path: decode attention over the
+    compacted cache, and one CentroidKV clustering round."""
+    import numpy as np
+    import torch
+
+    import_oracle = not args.no_cpu_baseline
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.decode:
+        wl = get_workload("structkv_128k_16l")
+        inp = make_inputs(wl, threads=_cores())
+        q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
+        L, B, Hq, Hkv, N, w, d, bud = (wl.n_layers, wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.n_keys, wl.window,
+                                       wl.head_dim, wl.kv_budget)
+        scores = K.kvsel_score(q, k, window=w, pool_kernel=wl.pool_kernel)
+        idx = K.kvsel_topk(scores, n_keys=N, window=w, budget=bud)
+        kc = K.kvsel_gather(k, idx).view(L * B, Hkv, bud, d)
+        vc = K.kvsel_gather(v, idx).view(L * B, Hkv, bud, d)
+        qd = q[:, :, :, w - 1].contiguous().view(L * B, Hq, d)  # the newest query of every head and layer
+        del k, v, q, scores
+        out = torch.empty((L * B, Hq, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, K.kvsel_decode_workspace_bytes(L * B, Hq, Hkv, d, bud)), dtype=torch.uint8,
+                         device=dev)
+        ms = timed(lambda: K.kvsel_decode_attention(qd, kc, vc, out=out, workspace=ws), stream, args.steps,
+                   args.warmup)
+        units = L * B * Hkv * bud
+        alg = 2 * units * d * 2 + L * B * Hq * d * (2 + 4)
+        cpu = None
+        if import_oracle:
+            import oracle
+
+            kh = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+            vh = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+            qh = qd.view(torch.int16).cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            n = 0
+            for r in range(L * B):
+                oracle.decode_attention(oracle.to_f64(qh[r], "bf16"), oracle.to_f64(kh[r], "bf16"),
+                                        oracle.to_f64(vh[r], "bf16"), None, 1.0 / d ** 0.5)
+                n += 1
+                if time.perf_counter() - t0 > 15.0:
+                    break
+            t = time.perf_counter() - t0
+            cpu = {"value": n * Hkv * bud / t, "unit": "keys/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{n} of {L * B} (layer, sequence) decode steps over {Hkv} KV heads x {bud} kept keys "
+                             f"in {t:.1f} s"}
+        line = {"metric": "decode attention over the compacted cache: kept keys attended/sec", "value": units / ms * 1e3,
+                "unit": "keys/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded; no dataset or weights)",
+                "config": {"workload": "structkv_128k_16l compacted (4096 kept per KV head, 16 layers)",
+                           "decode_batch": L * B, "q_heads": Hq, "kv_heads": Hkv, "keys": bud, "head_dim": d},
+                "roofline": {"bound": "hbm", "kernel": "kvsel_decode_attention (decode_kernel + combine)",
+                             "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                             "algorithmic_bytes": alg},
+                "cpu_baseline": cpu}
+        print(json.dumps(line))
+        return 0
+
+    wl = get_workload("batched_8x32k_ar1")
+    inp = make_inputs(wl, with_hidden=False, threads=_cores())
+    k, v = up(inp["k"]), up(inp["v"])
+    S = wl.n_layers * wl.batch * wl.n_kv_heads
+    n, d, chunk, ns, nr, rate = wl.n_keys, wl.head_dim, 64, 4, 32, 0.25
+    nm = K.csm_merge_count(rate, n, ns, nr)
+    ms = timed(lambda: K.kvsel_csm(k, v, chunk=chunk, n_sink=ns, n_recent=nr, n_merge=nm), stream, args.steps,
+               args.warmup)
+    n_out = n - nm
+    alg = 2 * S * n * d * 2 + 2 * S * n_out * d * 2 + S * n_out * 4
+    cpu = None
+    if import_oracle:
+        import oracle
+
+        kh = inp["k"].reshape(S, n, d)
+        vh = inp["v"].reshape(S, n, d)
+        t0 = time.perf_counter()
+        oracle.csm_round(oracle.to_f64(kh[0], "bf16"), oracle.to_f64(vh[0], "bf16"), None, chunk, ns, nr, nm)
+        t = time.perf_counter() - t0
+        cpu = {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"1 of {S} slabs ({n} tokens, one CSM round) in {t:.1f} s"}
+    line = {"metric": "CentroidKV chunked soft matching: cache tokens clustered/sec", "value": S * n / ms * 1e3,
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; no dataset or weights)",
+            "config": {"workload": "batched_8x32k_ar1 keys and values", "slabs": S, "tokens": n, "head_dim": d,
+                       "chunk": chunk, "n_sink": ns, "n_recent": nr, "rate": rate, "n_merge": nm},
+            "roofline": {"bound": "hbm", "kernel": "kvsel_csm (match + select + merge)",
+                         "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg},
+            "cpu_baseline": cpu}
     print(json.dumps(line))
     return 0
 

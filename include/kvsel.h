@@ -227,6 +227,68 @@ kvsel_status_t kvsel_topk_sinks(int32_t batch, int32_t rows, int64_t n_keys, int
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * CentroidKV chunked soft matching, one clustering round (page "Technische
+ * Samenvatting: CentroidKV", section "Methodologie": part 2 keeps sinks and
+ * recent tokens out of the partition, part 3 matches inside chunks and merges
+ * only the best-ranked matches, part 4 builds degree-weighted centroids).
+ *
+ * Per slab (layer, sequence, KV head) of n_tokens tokens, the middle
+ * [n_sink, n_tokens - n_recent) is cut into chunks of `chunk` tokens (even,
+ * 2..64; the last chunk may be shorter). In a chunk, offsets 0, 2, ... form
+ * set A and 1, 3, ... set B. Each A token's candidate is the B token of its
+ * chunk with the highest cosine similarity of keys (0 when a key is zero;
+ * ties to the lower position). The n_merge candidates of highest similarity
+ * (ties to the lower A position) merge into their B tokens; a cluster's key
+ * and value become the degree-weighted means of its members (fp32, rounded
+ * to bf16 to nearest even) and its degree their sum. Every other token is
+ * copied bit for bit. Survivors keep position order: n_out = n_tokens -
+ * n_merge rows per slab.
+ *
+ * k, v         device bf16 [n_slabs][n_tokens][head_dim], 16-byte aligned.
+ * degree       device int32 [n_slabs][n_tokens] (>= 1), or NULL for all 1.
+ * k_out, v_out device bf16 [n_slabs][n_out][head_dim]; degree_out device int32
+ *              [n_slabs][n_out]. Outputs must not overlap the inputs.
+ * score_out    device float [n_slabs][n_A] or NULL: each A token's best
+ *              similarity (-inf without a candidate); A tokens are numbered in
+ *              position order.
+ * match_out    device int32 [n_slabs][n_A] or NULL: that candidate's position
+ *              (-1 without one).
+ * chosen_out   device int32 [n_slabs][n_merge] or NULL: the merged A numbers,
+ *              ascending.
+ * n_merge must not exceed kvsel_csm_candidates(...). head_dim 64 or 128.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int64_t kvsel_csm_candidates(int64_t n_tokens, int32_t chunk, int32_t n_sink, int32_t n_recent);
+size_t kvsel_csm_workspace_bytes(int32_t n_slabs, int64_t n_tokens, int32_t chunk, int32_t n_sink, int32_t n_recent,
+                                 int32_t n_merge);
+kvsel_status_t kvsel_csm(int32_t n_slabs, int64_t n_tokens, int32_t head_dim, int32_t chunk, int32_t n_sink,
+                         int32_t n_recent, int32_t n_merge, const void* k, const void* v, const int32_t* degree,
+                         void* k_out, void* v_out, int32_t* degree_out, float* score_out, int32_t* match_out,
+                         int32_t* chosen_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention over a compacted cache (FastKV section 2B and StructKV
+ * section 3: decoding reads the kept cache; CentroidKV part 4: a centroid's
+ * degree enters the softmax as a log term).
+ *
+ * out[b][h][:] = sum_j p_j v[b][g][j][:], p = softmax over j of
+ *   scale * <q[b][h], k[b][g][j]> + ln degree[b][g][j],  g = h / (Hq / Hkv).
+ * q       device bf16 [batch][n_q_heads][head_dim] (one new query each).
+ * k, v    device bf16 [batch][n_kv_heads][n_keys][head_dim], 16-byte aligned.
+ * degree  device int32 [batch][n_kv_heads][n_keys] (>= 1), or NULL (no term).
+ * out     device float [batch][n_q_heads][head_dim].
+ * softmax_scale > 0, or <= 0 for 1/sqrt(head_dim). Fold layers into batch to
+ * run a step over every layer at once. head_dim 64 or 128; at most 8 query
+ * heads per KV head. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+size_t kvsel_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int64_t n_keys);
+kvsel_status_t kvsel_decode_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      int64_t n_keys, float softmax_scale, const void* q, const void* k, const void* v,
+                                      const int32_t* degree, float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * Compact the cache (FastKV section 2A: only the kept tokens are passed on;
  * section 2B / StructKV section 3: the kept KV entries are stored).
  *

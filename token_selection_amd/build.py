@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvsel.so")
 ARCH = "gfx950"
 
-SOURCES = ["score.hip", "stream.hip", "kres.hip", "topk.hip", "copy.hip", "pivot.hip", "kvsel_api.cpp"]
+SOURCES = ["score.hip", "stream.hip", "kres.hip", "topk.hip", "copy.hip", "pivot.hip", "centroid.hip", "decode.hip", "kvsel_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

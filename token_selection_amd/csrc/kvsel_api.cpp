@@ -361,6 +361,65 @@ kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t w
     return kvsel_topk_sinks(batch, rows, n_keys, window, budget, 0, scores, idx, workspace, workspace_bytes, stream);
 }
 
+int64_t kvsel_csm_candidates(int64_t n_tokens, int32_t chunk, int32_t n_sink, int32_t n_recent) {
+    if (n_tokens < 1 || n_tokens >= kMaxKeys || chunk < 2 || chunk > 64 || chunk % 2 || n_sink < 0 || n_recent < 0 ||
+        (int64_t)n_sink + n_recent > n_tokens)
+        return -1;
+    return kvsel::csm_candidates(n_tokens, chunk, n_sink, n_recent);
+}
+
+size_t kvsel_csm_workspace_bytes(int32_t n_slabs, int64_t n_tokens, int32_t chunk, int32_t n_sink, int32_t n_recent,
+                                 int32_t n_merge) {
+    const int64_t cand = kvsel_csm_candidates(n_tokens, chunk, n_sink, n_recent);
+    if (n_slabs < 1 || n_slabs > 65535 || cand < 0 || n_merge < 0 || n_merge > cand) return 0;
+    return kvsel::csm_workspace_bytes(n_slabs, n_tokens, chunk, n_sink, n_recent, n_merge);
+}
+
+kvsel_status_t kvsel_csm(int32_t n_slabs, int64_t n_tokens, int32_t head_dim, int32_t chunk, int32_t n_sink,
+                         int32_t n_recent, int32_t n_merge, const void* k, const void* v, const int32_t* degree,
+                         void* k_out, void* v_out, int32_t* degree_out, float* score_out, int32_t* match_out,
+                         int32_t* chosen_out, void* workspace, size_t workspace_bytes, void* stream) {
+    const int64_t cand = kvsel_csm_candidates(n_tokens, chunk, n_sink, n_recent);
+    if (n_slabs < 1 || n_slabs > 65535 || cand < 0 || n_merge < 0 || n_merge > cand) return KVSEL_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
+    if (!k || !v || !k_out || !v_out || !degree_out) return KVSEL_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out)) return KVSEL_ERR_INVALID_ARG;
+    const size_t need = kvsel::csm_workspace_bytes(n_slabs, n_tokens, chunk, n_sink, n_recent, n_merge);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
+    return from_hip(kvsel::launch_csm(n_slabs, n_tokens, head_dim, chunk, n_sink, n_recent, n_merge,
+                                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), degree,
+                                      static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), degree_out,
+                                      score_out, match_out, chosen_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvsel_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int64_t n_keys) {
+    if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_keys < 1 || n_keys >= kMaxKeys ||
+        (head_dim != 64 && head_dim != 128) || (int64_t)batch * n_kv_heads > 65535 ||
+        n_q_heads / n_kv_heads > kvsel::decode_max_group())
+        return 0;
+    return kvsel::decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_keys);
+}
+
+kvsel_status_t kvsel_decode_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      int64_t n_keys, float softmax_scale, const void* q, const void* k, const void* v,
+                                      const int32_t* degree, float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_keys < 1 || n_keys >= kMaxKeys ||
+        (int64_t)batch * n_kv_heads > 65535 || (int64_t)batch * n_q_heads > 0x7fffffff || !isfinite(softmax_scale))
+        return KVSEL_ERR_INVALID_ARG;
+    if ((head_dim != 64 && head_dim != 128) || n_q_heads / n_kv_heads > kvsel::decode_max_group())
+        return KVSEL_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !out || !aligned16(k) || !aligned16(v)) return KVSEL_ERR_INVALID_ARG;
+    const size_t need = kvsel::decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_keys);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
+    return from_hip(kvsel::launch_decode(batch, n_q_heads, n_kv_heads, head_dim, n_keys, scale,
+                                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(v), degree, out, workspace,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 kvsel_status_t kvsel_gather(int32_t n_layers, int32_t batch, int32_t n_heads, int32_t idx_heads, int32_t budget,
                             int64_t n_src_rows, int64_t row_bytes, const void* src,
                             const int64_t src_strides_bytes[4], const int32_t* idx, void* dst, void* stream) {

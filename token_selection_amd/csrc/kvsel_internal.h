@@ -137,6 +137,21 @@ size_t topk_workspace_bytes(int32_t rows, int64_t n_prefix);
 hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, int32_t n_sink,
                        const float* scores, int32_t* idx, void* workspace, hipStream_t stream);
 
+// CentroidKV chunked soft matching (centroid.hip).
+int64_t csm_candidates(int64_t n, int32_t chunk, int32_t n_sink, int32_t n_recent);
+size_t csm_workspace_bytes(int32_t S, int64_t n, int32_t chunk, int32_t n_sink, int32_t n_recent, int32_t n_merge);
+hipError_t launch_csm(int32_t S, int64_t n, int32_t d, int32_t chunk, int32_t n_sink, int32_t n_recent,
+                      int32_t n_merge, const uint16_t* k, const uint16_t* v, const int32_t* degree, uint16_t* k_out,
+                      uint16_t* v_out, int32_t* degree_out, float* score_out, int32_t* match_out,
+                      int32_t* chosen_out, void* workspace, hipStream_t stream);
+
+// Decode attention over a compacted cache (decode.hip).
+int decode_max_group();
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n);
+hipError_t launch_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, float scale, const uint16_t* q,
+                         const uint16_t* k, const uint16_t* v, const int32_t* degree, float* out, void* workspace,
+                         hipStream_t stream);
+
 hipError_t launch_gather(int32_t L, int32_t B, int32_t H, int32_t idx_heads, int32_t budget, int64_t n_src_rows,
                          int64_t row_bytes, const void* src, const int64_t s[4], const int32_t* idx, void* dst,
                          hipStream_t stream);

@@ -43,6 +43,11 @@ EXPORTED = (
     "kvsel_topk",
     "kvsel_topk_sinks",
     "kvsel_gather",
+    "kvsel_csm_candidates",
+    "kvsel_csm_workspace_bytes",
+    "kvsel_csm",
+    "kvsel_decode_workspace_bytes",
+    "kvsel_decode_attention",
     "kvsel_status_string",
     "kvsel_version",
 )
@@ -112,6 +117,16 @@ def load_library() -> ctypes.CDLL:
     lib.kvsel_topk_sinks.restype = i32
     lib.kvsel_gather.argtypes = [i32, i32, i32, i32, i32, i64, i64, vp, ctypes.POINTER(ctypes.c_int64), vp, vp, vp]
     lib.kvsel_gather.restype = i32
+    lib.kvsel_csm_candidates.argtypes = [i64, i32, i32, i32]
+    lib.kvsel_csm_candidates.restype = i64
+    lib.kvsel_csm_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.kvsel_csm_workspace_bytes.restype = sz
+    lib.kvsel_csm.argtypes = [i32, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvsel_csm.restype = i32
+    lib.kvsel_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i64]
+    lib.kvsel_decode_workspace_bytes.restype = sz
+    lib.kvsel_decode_attention.argtypes = [i32, i32, i32, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kvsel_decode_attention.restype = i32
     lib.kvsel_status_string.argtypes = [i32]
     lib.kvsel_status_string.restype = ctypes.c_char_p
     lib.kvsel_version.argtypes = []
@@ -310,6 +325,84 @@ def kvsel_pivot_layer(mean_entropy, mean_sparsity, *, min_drop: float, min_rise:
     out = ctypes.c_int32(-1)
     _check(lib.kvsel_pivot_layer(len(e), ea, sa, min_drop, min_rise, ctypes.byref(out)), "kvsel_pivot_layer")
     return int(out.value)
+
+
+# ---------------------------------------------------------------------------
+# CentroidKV chunked soft matching, decode attention
+# ---------------------------------------------------------------------------
+def csm_merge_count(rate: float, n_tokens: int, n_sink: int, n_recent: int) -> int:
+    """Merges of one round at compression ratio ``rate`` (a fraction of the
+    middle tokens; the progressive schedule lowers it linearly per round)."""
+    return int(math.floor(rate * (n_tokens - n_sink - n_recent) + 1e-9))
+
+
+def kvsel_csm(k: torch.Tensor, v: torch.Tensor, degree: Optional[torch.Tensor] = None, *, chunk: int,
+              n_sink: int, n_recent: int, n_merge: int, with_decisions: bool = False, stream=None):
+    """One CSM round over the slabs of k, v ([..., n, d] bf16, contiguous):
+    returns (k_out, v_out, degree_out) with n - n_merge rows per slab, plus
+    (score, match, chosen) with ``with_decisions``."""
+    lib = load_library()
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or not k.is_contiguous() or not v.is_contiguous():
+        raise ValueError("k and v must be contiguous bf16 tensors")
+    if k.shape != v.shape or k.dim() < 2:
+        raise ValueError("k and v must have the same [..., n, d] shape")
+    n, d = k.shape[-2], k.shape[-1]
+    lead = tuple(k.shape[:-2])
+    S = int(math.prod(lead)) if lead else 1
+    if degree is not None and (degree.dtype != torch.int32 or not degree.is_contiguous() or
+                               tuple(degree.shape) != lead + (n,)):
+        raise ValueError("degree must be a contiguous int32 [..., n] tensor")
+    cand = int(lib.kvsel_csm_candidates(n, chunk, n_sink, n_recent))
+    n_out = n - n_merge
+    dev = k.device
+    k_out = torch.empty(lead + (n_out, d), dtype=k.dtype, device=dev)
+    v_out = torch.empty_like(k_out)
+    deg_out = torch.empty(lead + (n_out,), dtype=torch.int32, device=dev)
+    n_a = cand + (1 if cand >= 0 and (n - n_sink - n_recent) % chunk == 1 else 0)
+    score = match = chosen = None
+    if with_decisions:
+        score = torch.empty(lead + (max(n_a, 0),), dtype=torch.float32, device=dev)
+        match = torch.empty(lead + (max(n_a, 0),), dtype=torch.int32, device=dev)
+        chosen = torch.empty(lead + (max(n_merge, 0),), dtype=torch.int32, device=dev)
+    need = int(lib.kvsel_csm_workspace_bytes(S, n, chunk, n_sink, n_recent, n_merge))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.kvsel_csm(S, n, d, chunk, n_sink, n_recent, n_merge, _ptr(k), _ptr(v), _ptr(degree), _ptr(k_out),
+                         _ptr(v_out), _ptr(deg_out), _ptr(score), _ptr(match), _ptr(chosen), _ptr(ws), ws.numel(),
+                         _stream(dev, stream)), "kvsel_csm")
+    if with_decisions:
+        return k_out, v_out, deg_out, score, match, chosen
+    return k_out, v_out, deg_out
+
+
+def kvsel_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_keys: int) -> int:
+    return int(load_library().kvsel_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_keys))
+
+
+def kvsel_decode_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, degree: Optional[torch.Tensor] = None,
+                           *, softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step: q [B, Hq, d] bf16 against k, v [B, Hkv, n, d] bf16
+    (and degree [B, Hkv, n] int32) -> out [B, Hq, d] float32."""
+    lib = load_library()
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("q, k and v must be contiguous bf16 tensors")
+    B, Hq, d = q.shape
+    _, Hkv, n, _ = k.shape
+    if tuple(k.shape) != (B, Hkv, n, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, n, d]")
+    if degree is not None and (degree.dtype != torch.int32 or not degree.is_contiguous() or
+                               tuple(degree.shape) != (B, Hkv, n)):
+        raise ValueError("degree must be a contiguous int32 [B, Hkv, n] tensor")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    need = int(lib.kvsel_decode_workspace_bytes(B, Hq, Hkv, d, n))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.kvsel_decode_attention(B, Hq, Hkv, d, n, softmax_scale, _ptr(q), _ptr(k), _ptr(v), _ptr(degree),
+                                      _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device, stream)),
+           "kvsel_decode_attention")
+    return out
 
 
 # ---------------------------------------------------------------------------
