@@ -48,6 +48,33 @@ struct Frag {
     bf16x8 v[kKB][D / 16];
 };
 
+// Pass 1 without statistics: each lane's running (reference, sum) of its row
+// in every row block, over the keys of its lane half, held in registers for
+// the whole segment (the halves and the waves merge when the segment ends).
+template <int RBN>
+struct RowState {
+    float m[RBN], z[RBN];
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int rb = 0; rb < RBN; ++rb) {
+            m[rb] = kNegBig;
+            z[rb] = 0.f;
+        }
+    }
+    // Slot 0 is the current row block's; after RBN rotations every row
+    // block is back in its own slot (static register indices only).
+    __device__ __forceinline__ void rotate() {
+        const float m0 = m[0], z0 = z[0];
+#pragma unroll
+        for (int rb = 0; rb + 1 < RBN; ++rb) {
+            m[rb] = m[rb + 1];
+            z[rb] = z[rb + 1];
+        }
+        m[RBN - 1] = m0;
+        z[RBN - 1] = z0;
+    }
+};
+
 // Position in a work-group's sequence of chunks.
 struct Cursor {
     int seg;    // segment index (slab * spp + part)
@@ -162,15 +189,38 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
 }
 
 // Pass 1 on one chunk: merge this wave's (reference, sum) of every row into
-// its running state.
+// its running state (registers without statistics, LDS with them).
 template <int D, int RBN, bool ST>
 __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamArgs& a, const Frag<D>& f,
-                                            const Cursor& c, int wave, int col, int hf) {
+                                            const Cursor& c, int wave, int col, int hf, RowState<RBN>& rs) {
     constexpr int KS = D / 16;
     constexpr int QST = D + 8;
     const int kbase = c.first + wave * kWaveKeys;
     if (kbase >= a.N) return;  // the chunk ends before this wave's keys
     const bool edge = kbase + kWaveKeys > a.Np;  // reaches the window (causal mask) or the end
+    if constexpr (!ST) {
+#pragma unroll 1
+        for (int rb = 0; rb < a.rbn; ++rb) {
+            bf16x8 qf[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[ks] = *reinterpret_cast<const bf16x8*>(sm.q + (rb * 32 + col) * QST + ks * 16 + hf * 8);
+            // lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
+            float m, z;
+            if (edge) {
+                const int row = rb * 32 + col;
+                const int lim = row < a.R ? a.Np + row % a.w : -1;
+                z = pass1_max<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m);
+            } else {
+                z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
+                if (__any(!(z < kOverflow))) z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
+            }
+            merge(rs.m[0], rs.z[0], m, z);
+            rs.rotate();
+        }
+        for (int rb = a.rbn; rb < RBN; ++rb) rs.rotate();
+        return;
+    }
 #pragma unroll 1
     for (int rb = 0; rb < a.rbn; ++rb) {
         bf16x8 qf[KS];
@@ -196,21 +246,6 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
                 Moments sa{st.z, st.w};
                 merge_st(st.x, st.y, sa, m, z, mo);
                 sm.st[wave][rb * 32 + col] = make_float4(st.x, st.y, sa.s, sa.q);
-            }
-        } else {
-            if (edge) {
-                const int row = rb * 32 + col;
-                const int lim = row < a.R ? a.Np + row % a.w : -1;
-                z = pass1_max<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m);
-            } else {
-                z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
-                if (__any(!(z < kOverflow))) z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
-            }
-            merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));  // the two lane halves: same row, other keys
-            if (hf == 0) {
-                float2 st = sm.st[wave][rb * 32 + col];
-                merge(st.x, st.y, m, z);
-                sm.st[wave][rb * 32 + col] = st;
             }
         }
     }
@@ -287,8 +322,20 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
 
 // Pass 1, end of a segment: merge the waves' states and publish the partials.
 template <int D, int RBN, bool ST>
-__device__ __forceinline__ void pass1_finish(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int tid) {
+__device__ __forceinline__ void pass1_finish(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int tid,
+                                             RowState<RBN>& rs) {
     constexpr int RP = RBN * 32;
+    if constexpr (!ST) {
+        // the two lane halves (same row, other keys), then this wave's row states to LDS
+        const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+        for (int rb = 0; rb < RBN; ++rb) {
+            float m = rs.m[rb], z = rs.z[rb];
+            merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
+            if (lane < 32) sm.st[wave][rb * 32 + lane] = make_float2(m, z);
+        }
+        rs.reset();
+    }
     __syncthreads();
     for (int row = tid; row < RP; row += 256) {
         if constexpr (ST) {
@@ -326,17 +373,17 @@ __device__ __forceinline__ void pass2_finish(Smem<D, RBN, true>& sm, const Strea
 // Returns false once the work-group's sequence ends.
 template <int D, int RBN, int PASS, bool ST>
 __device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, const StreamArgs& a, Cursor& cur, Frag<D>& f,
-                                     Frag<D>& g, int tid, int wave, int col, int hf) {
+                                     Frag<D>& g, int tid, int wave, int col, int hf, RowState<RBN>& rs) {
     const Cursor nx = advance(a, cur);
     // Issued on every step (the last one re-reads the current chunk): with a
     // fixed number of loads in flight the wait for `f` leaves `g`'s in flight.
     load_chunk<D>(g, a, nx.seg >= 0 ? nx : cur, wave, col, hf);
     if (PASS == 1)
-        pass1_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf);
+        pass1_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf, rs);
     else
         pass2_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf);
     if (nx.seg != cur.seg) {
-        if (PASS == 1) pass1_finish<D, RBN, ST>(sm, a, cur.seg, tid);
+        if (PASS == 1) pass1_finish<D, RBN, ST>(sm, a, cur.seg, tid, rs);
         if constexpr (ST && PASS == 2) pass2_finish<D, RBN>(sm, a, cur.seg, tid);
         if (nx.seg < 0) return false;
         stage<D, RBN, PASS, ST>(sm, a, nx.seg, tid);
@@ -365,12 +412,14 @@ stream_kernel(StreamArgs a) {
     }
     if (cur.seg < 0) return;
     Frag<D> fa, fb;
+    RowState<RBN> rs;
+    rs.reset();
     load_chunk<D>(fa, a, cur, wave, col, hf);
     stage<D, RBN, PASS, ST>(sm, a, cur.seg, tid);
 
     for (;;) {
-        if (!step<D, RBN, PASS, ST>(sm, a, cur, fa, fb, tid, wave, col, hf)) break;
-        if (!step<D, RBN, PASS, ST>(sm, a, cur, fb, fa, tid, wave, col, hf)) break;
+        if (!step<D, RBN, PASS, ST>(sm, a, cur, fa, fb, tid, wave, col, hf, rs)) break;
+        if (!step<D, RBN, PASS, ST>(sm, a, cur, fb, fa, tid, wave, col, hf, rs)) break;
     }
 }
 
