@@ -48,31 +48,41 @@ struct DecGeom {
 
 __device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// EL consecutive bf16 elements (16 or 8 bytes) as fp32.
+// EL consecutive bf16 elements kept as raw 32-bit words until use.
 template <int EL>
-__device__ __forceinline__ void load_row_slice(const uint16_t* p, float (&x)[EL]) {
+struct Slice {
+    uint32_t w[EL / 2];
+};
+
+template <int EL>
+__device__ __forceinline__ Slice<EL> load_slice(const uint16_t* p) {
+    Slice<EL> s;
     if constexpr (EL == 8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(p);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            x[2 * h] = bf(ws[h] & 0xFFFFu);
-            x[2 * h + 1] = bf(ws[h] >> 16);
-        }
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        s.w[0] = x.x;
+        s.w[1] = x.y;
+        s.w[2] = x.z;
+        s.w[3] = x.w;
     } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(p);
-        x[0] = bf(w.x & 0xFFFFu);
-        x[1] = bf(w.x >> 16);
-        x[2] = bf(w.y & 0xFFFFu);
-        x[3] = bf(w.y >> 16);
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        s.w[0] = x.x;
+        s.w[1] = x.y;
     }
+    return s;
 }
 
-// Waves per SIMD the register state allows without spills: 4 while the
-// query slice, value sums and a block's rows fit in 128 registers, else 2.
+// element e of a slice as fp32
+template <int EL>
+__device__ __forceinline__ float elem(const Slice<EL>& s, int e) {
+    const uint32_t w = s.w[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+// Waves per SIMD the register state allows without spills (128, 168 or 256
+// registers a wave).
 template <int D, int G>
 constexpr int dec_waves_per_eu() {
-    return (D == 128 ? G <= 2 : G <= 4) ? 4 : 2;
+    return D == 128 ? (G <= 2 ? 4 : G <= 4 ? 3 : 2) : (G <= 4 ? 4 : 3);
 }
 
 template <int D, int G>
@@ -114,25 +124,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
         for (int e = 0; e < EL; ++e) acc[gg][e] = 0.f;
     }
     for (int64_t blk = key0 + (int64_t)wave * kBlock; blk < key1; blk += kDecWaves * kBlock) {
-        // the block's value slices load while its logits are formed
-        float xv[kT][EL];
+        // the block's key and value slices all load first (raw words until use)
+        Slice<EL> xk[kT], xv[kT];
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
             const int64_t row = min(blk + 4 * t + r, key1 - 1);  // rows past the end carry weight 0
-            load_row_slice<EL>(vb + row * D + sl * EL, xv[t]);
+            xk[t] = load_slice<EL>(kb + row * D + sl * EL);
+            xv[t] = load_slice<EL>(vb + row * D + sl * EL);
         }
         // --- logits of rows blk + 4t + r: the lane's partial dot products, summed over its 16 lanes
         float s[kT][G];
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
-            const int64_t row = min(blk + 4 * t + r, key1 - 1);
-            float x[EL];
-            load_row_slice<EL>(kb + row * D + sl * EL, x);
 #pragma unroll
             for (int gg = 0; gg < G; ++gg) {
                 float a = 0.f;
 #pragma unroll
-                for (int e = 0; e < EL; ++e) a += qv[gg][e] * x[e];
+                for (int e = 0; e < EL; ++e) a += qv[gg][e] * elem<EL>(xk[t], e);
                 s[t][gg] = a;
             }
         }
@@ -188,9 +196,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
 #pragma unroll
         for (int t = 0; t < kT; ++t)
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg)
+            for (int e = 0; e < EL; ++e) {
+                const float x = elem<EL>(xv[t], e);
 #pragma unroll
-                for (int e = 0; e < EL; ++e) acc[gg][e] += s[t][gg] * xv[t][e];
+                for (int gg = 0; gg < G; ++gg) acc[gg][e] += s[t][gg] * x;
+            }
     }
     // --- the four row sets of a wave, then the four waves
 #pragma unroll
@@ -264,16 +274,22 @@ __global__ void decode_combine_kernel(DecGeom g, const float* part_m, const floa
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecGeom plan(int32_t B, int32_t Hq, int32_t Hkv, int64_t n, float scale) {
+// Resident work-groups per CU of decode_kernel<d, G> (a work-group has one
+// wave per SIMD): dec_waves_per_eu on the host.
+int resident_per_cu(int d, int G) { return d == 128 ? (G <= 2 ? 4 : G <= 4 ? 3 : 2) : (G <= 4 ? 4 : 3); }
+
+DecGeom plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, float scale, int n_cu) {
     DecGeom g;
     g.B = B;
     g.Hq = Hq;
     g.Hkv = Hkv;
     g.G = Hq / Hkv;
     g.n = n;
-    // about 1024 work-groups, each at least 4 blocks of 64 keys
+    // one full wave of resident work-groups (a second, partial wave would run
+    // at a fraction of the occupancy), each split at least 256 keys
     const int64_t units = (int64_t)B * Hkv;
-    int64_t s = (1024 + units - 1) / units;
+    const int64_t target = (int64_t)n_cu * resident_per_cu(d, g.G);
+    int64_t s = (target + units - 1) / units;
     const int64_t max_s = (n + 255) / 256;
     if (s > max_s) s = max_s;
     if (s < 1) s = 1;
@@ -312,16 +328,16 @@ bool launch_g(const DecGeom& g, const uint16_t* q, const uint16_t* k, const uint
 
 int decode_max_group() { return kMaxG; }
 
-size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n) {
-    const DecGeom g = plan(B, Hq, Hkv, n, 1.f);
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, int n_cu) {
+    const DecGeom g = plan(B, Hq, Hkv, d, n, 1.f, n_cu);
     const size_t rows = (size_t)g.splits * B * Hq;
     return align256(rows * sizeof(float)) * 2 + align256(rows * d * sizeof(float));
 }
 
 hipError_t launch_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, float scale, const uint16_t* q,
                          const uint16_t* k, const uint16_t* v, const int32_t* degree, float* out, void* workspace,
-                         hipStream_t st) {
-    const DecGeom g = plan(B, Hq, Hkv, n, scale);
+                         int n_cu, hipStream_t st) {
+    const DecGeom g = plan(B, Hq, Hkv, d, n, scale, n_cu);
     const size_t rows = (size_t)g.splits * B * Hq;
     char* ws = static_cast<char*>(workspace);
     float* pm = reinterpret_cast<float*>(ws);

@@ -398,7 +398,7 @@ size_t kvsel_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_
         (head_dim != 64 && head_dim != 128) || (int64_t)batch * n_kv_heads > 65535 ||
         n_q_heads / n_kv_heads > kvsel::decode_max_group())
         return 0;
-    return kvsel::decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_keys);
+    return kvsel::decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_keys, device_cu_count());
 }
 
 kvsel_status_t kvsel_decode_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -411,12 +411,13 @@ kvsel_status_t kvsel_decode_attention(int32_t batch, int32_t n_q_heads, int32_t 
     if ((head_dim != 64 && head_dim != 128) || n_q_heads / n_kv_heads > kvsel::decode_max_group())
         return KVSEL_ERR_UNSUPPORTED;
     if (!q || !k || !v || !out || !aligned16(k) || !aligned16(v)) return KVSEL_ERR_INVALID_ARG;
-    const size_t need = kvsel::decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_keys);
+    const int n_cu = device_cu_count();
+    const size_t need = kvsel::decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_keys, n_cu);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
     const float scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / sqrt((double)head_dim));
     return from_hip(kvsel::launch_decode(batch, n_q_heads, n_kv_heads, head_dim, n_keys, scale,
                                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                         static_cast<const uint16_t*>(v), degree, out, workspace,
+                                         static_cast<const uint16_t*>(v), degree, out, workspace, n_cu,
                                          static_cast<hipStream_t>(stream)));
 }
 

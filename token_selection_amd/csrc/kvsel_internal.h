@@ -147,10 +147,10 @@ hipError_t launch_csm(int32_t S, int64_t n, int32_t d, int32_t chunk, int32_t n_
 
 // Decode attention over a compacted cache (decode.hip).
 int decode_max_group();
-size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n);
+size_t decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, int n_cu);
 hipError_t launch_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, float scale, const uint16_t* q,
                          const uint16_t* k, const uint16_t* v, const int32_t* degree, float* out, void* workspace,
-                         hipStream_t stream);
+                         int n_cu, hipStream_t stream);
 
 hipError_t launch_gather(int32_t L, int32_t B, int32_t H, int32_t idx_heads, int32_t budget, int64_t n_src_rows,
                          int64_t row_bytes, const void* src, const int64_t s[4], const int32_t* idx, void* dst,
