@@ -259,7 +259,9 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
     constexpr int QST = D + 8;
     const int kbase = c.first + wave * kWaveKeys;
     if (kbase >= a.n_range) return;  // no keys of this pass in this wave's range
-    float cs0 = 0.f, cs1 = 0.f;
+    float cs[kKB];
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) cs[kb] = 0.f;
 #pragma unroll 1
     for (int rb = 0; rb < a.rbn; ++rb) {
         bf16x8 qf[KS];
@@ -276,23 +278,19 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
             lr[4 * u + 3] = t.w;
         }
         // lane holds key kbase + kb*32 + col and rows rb*32 + tile_row(v, hf)
-        const f32x16 x0 = logits<KS>(qf, f.v[0]);
-        const f32x16 x1 = logits<KS>(qf, f.v[1]);  // in the matrix core while x0 is exponentiated
-        float s0 = 0.f, s1 = 0.f;
+        f32x16 x[kKB];
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-            s0 += fexp2(x0[v] * a.c - lr[v]);
-            s1 += fexp2(x0[v + 1] * a.c - lr[v + 1]);
-        }
-        cs0 += s0 + s1;
-        s0 = 0.f;
-        s1 = 0.f;
+        for (int kb = 0; kb < kKB; ++kb) x[kb] = logits<KS>(qf, f.v[kb]);
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-            s0 += fexp2(x1[v] * a.c - lr[v]);
-            s1 += fexp2(x1[v + 1] * a.c - lr[v + 1]);
+        for (int kb = 0; kb < kKB; ++kb) {
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                s0 += fexp2(x[kb][v] * a.c - lr[v]);
+                s1 += fexp2(x[kb][v + 1] * a.c - lr[v + 1]);
+            }
+            cs[kb] += s0 + s1;
         }
-        cs1 += s0 + s1;
         if constexpr (ST) {
             // key-major tiles: lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
             const int row = rb * 32 + col;
@@ -312,12 +310,12 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
         }
     }
     const int slab = c.seg / a.spp;
-    const float v0 = cs0 + __shfl_xor(cs0, 32);
-    const float v1 = cs1 + __shfl_xor(cs1, 32);
-    const int j0 = kbase + col;
-    const int j1 = kbase + 32 + col;
-    if (hf == 0 && j0 < a.Np) a.raw[(int64_t)slab * a.Np + j0] = v0 * a.invG;
-    if (hf == 0 && j1 < a.Np) a.raw[(int64_t)slab * a.Np + j1] = v1 * a.invG;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
+        const float val = cs[kb] + __shfl_xor(cs[kb], 32);
+        const int j = kbase + kb * 32 + col;
+        if (hf == 0 && j < a.Np) a.raw[(int64_t)slab * a.Np + j] = val * a.invG;
+    }
 }
 
 // Pass 1, end of a segment: merge the waves' states and publish the partials.
