@@ -65,10 +65,12 @@ def _cores() -> int:
     return max(1, min(16, n))
 
 
-def cpu_baseline(wl, inp, budget_s: float = 15.0) -> dict:
+def cpu_baseline(wl, inp, budget_s: float = 15.0, mode: str = "two-pass", lse=None, small_p=None) -> dict:
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: the first n layers of every sequence and KV head through
-    score -> accumulate -> select -> gather, n chosen for ~budget_s seconds."""
+    score -> accumulate -> select -> gather (with the LSE handed in, or plus
+    the row statistics, as the timed mode does), n chosen for ~budget_s
+    seconds."""
     import oracle
 
     cores = _cores()
@@ -76,7 +78,10 @@ def cpu_baseline(wl, inp, budget_s: float = 15.0) -> dict:
     def run(n):
         t0 = time.perf_counter()
         oracle.pipeline(inp["q"][:n], inp["k"][:n], inp["v"][:n], dtype=wl.dtype, window=wl.window,
-                        pool_kernel=wl.pool_kernel, kv_budget=wl.kv_budget, threads=cores)
+                        pool_kernel=wl.pool_kernel, kv_budget=wl.kv_budget, threads=cores,
+                        lse_in=None if lse is None else lse[:n])
+        if mode == "stats":
+            oracle.row_stats_all(inp["q"][:n], inp["k"][:n], wl.dtype, small_p, threads=cores)
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -89,7 +94,8 @@ def cpu_baseline(wl, inp, budget_s: float = 15.0) -> dict:
     units = n * wl.batch * wl.n_kv_heads * wl.n_keys
     return {"value": units / t, "unit": "keys/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {wl.n_layers} layers x {wl.batch} seq x {wl.n_kv_heads} KV heads x {wl.n_keys} keys "
-                      f"(score, layer sum, select, K/V gather) in {t:.1f} s on {cores} threads"}
+                      f"(score{' from the given LSE' if lse is not None else ''}, layer sum, select, K/V gather"
+                      f"{', row statistics' if mode == 'stats' else ''}) in {t:.1f} s on {cores} threads"}
 
 
 def main() -> int:
@@ -226,7 +232,9 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, inp)
+        cpu = cpu_baseline(wl, inp, mode="stats" if args.stats else "lse-in" if lse_in is not None else "two-pass",
+                           lse=None if lse_in is None else lse_in.cpu().numpy().astype(np.float64),
+                           small_p=small_p)
 
     line = {
         "metric": "keys scored+selected/sec and achieved HBM GB/s (% of peak), 128K ctx",

@@ -139,8 +139,9 @@ kvsel_status_t kvsel_score_lse(const kvsel_score_desc_t* desc, const void* q_win
  * sum_p2   device float[L][B][Hq][w]: sum_j p_j^2 (the row's variance of
  *          weights is sum_p2 / n - 1 / n^2 with n = N - w + i + 1).
  * n_below  device int32[L][B][Hq][w]: the number of keys the row sees with
- *          p_j < small_p (decided in fp32 on the logit: x < (log2(small_p) +
- *          LSE2) / c; keys within rounding of the threshold may fall either way).
+ *          p_j < small_p (decided in fp32 on the exponent: c*x - LSE2 <
+ *          log2(small_p), c = scale*log2(e); keys within rounding of the
+ *          threshold may fall either way).
  * Only the streaming path computes them: bf16, head_dim 64/128, G*w <= 256;
  * other shapes return UNSUPPORTED. Both passes read every key.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.

@@ -14,8 +14,9 @@
 // With ST (the pivot statistics of StructKV section 2) pass 1 also carries
 // each row's sum of e*x and e^2 (tile32.h), the merge turns them into the
 // row's entropy and sum of p^2, and pass 2 runs over all N keys and also counts
-// the keys each row sees with p below a threshold, from key-major tiles whose
-// lanes are rows.
+// the keys each row sees with p below a threshold: the exponent it already
+// has decides (c*x - LSE2 < log2 threshold), into packed per-lane counters
+// that are summed over the lanes once per segment.
 //
 // No work-group waits for another: every slab is cut into segments of whole
 // 256-key chunks, work-group g takes segments g, g + grid, ..., and while it
@@ -72,6 +73,35 @@ struct RowState {
         }
         m[RBN - 1] = m0;
         z[RBN - 1] = z0;
+    }
+};
+
+// Pass 2 with statistics: per lane, for every row block and result register
+// v (row rb*32 + tile_row(v, half)), how many of the lane's keys had p below
+// the threshold: 8-bit fields, four to a register, in rotating slots like
+// RowState. A field grows by at most kKB per chunk and segments hold at most
+// kMaxSegChunks chunks, so it cannot overflow before the segment's flush.
+constexpr int kMaxSegChunks = 127;
+
+template <int RBN>
+struct CountState {
+    uint32_t c[RBN][4];
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int rb = 0; rb < RBN; ++rb)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) c[rb][w] = 0u;
+    }
+    __device__ __forceinline__ void rotate() {
+        uint32_t c0[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) c0[w] = c[0][w];
+#pragma unroll
+        for (int rb = 0; rb + 1 < RBN; ++rb)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) c[rb][w] = c[rb + 1][w];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) c[RBN - 1][w] = c0[w];
     }
 };
 
@@ -132,7 +162,6 @@ struct Smem {
     uint16_t q[RP * QST];
     State st[kWaves][RP];     // pass 1: running (reference, sum[, s, q]) per wave and row
     float lse[RP];            // pass 2: row LSE2 (+inf on padded rows)
-    float thr[SP];            // pass 2 with ST: logit below which a key's p is under the threshold
     uint32_t cnt[kWaves][SP]; // pass 2 with ST: per wave and row, keys counted so far
 };
 
@@ -173,7 +202,7 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
         for (int row = tid; row < RP; row += 256) {
             const float l2 = row < a.R ? a.lse2[(int64_t)slab * RP + row] : INFINITY;
             sm.lse[row] = l2;
-            if constexpr (ST) sm.thr[row] = (a.l2tau + l2) / a.c;  // c*x - LSE2 < log2(tau)  <=>  x < thr
+
         }
         if constexpr (ST)
             for (int i = tid; i < kWaves * RP; i += 256) (&sm.cnt[0][0])[i] = 0u;
@@ -254,7 +283,7 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
 // Pass 2 on one chunk: raw score of each of this wave's prefix keys.
 template <int D, int RBN, bool ST>
 __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamArgs& a, const Frag<D>& f,
-                                            const Cursor& c, int wave, int col, int hf) {
+                                            const Cursor& c, int wave, int col, int hf, CountState<RBN>& cn) {
     constexpr int KS = D / 16;
     constexpr int QST = D + 8;
     const int kbase = c.first + wave * kWaveKeys;
@@ -281,34 +310,61 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
         f32x16 x[kKB];
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb) x[kb] = logits<KS>(qf, f.v[kb]);
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
-            float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-                s0 += fexp2(x[kb][v] * a.c - lr[v]);
-                s1 += fexp2(x[kb][v + 1] * a.c - lr[v + 1]);
-            }
-            cs[kb] += s0 + s1;
-        }
-        if constexpr (ST) {
-            // key-major tiles: lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
-            const int row = rb * 32 + col;
-            const float thr = sm.thr[row];
-            const bool edge = kbase + kWaveKeys > a.Np;  // reaches the window (causal mask) or the end
-            const int lim = row < a.R ? a.Np + row % a.w : -1;
-            uint32_t n = 0;
+        if constexpr (!ST) {
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb) {
-                const f32x16 y = logits<KS>(f.v[kb], qf);
+                float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    n += (y[v] < thr && (!edge || kbase + kb * 32 + tile_row(v, hf) <= lim)) ? 1u : 0u;
+                for (int v = 0; v < 16; v += 2) {
+                    s0 += fexp2(x[kb][v] * a.c - lr[v]);
+                    s1 += fexp2(x[kb][v + 1] * a.c - lr[v + 1]);
+                }
+                cs[kb] += s0 + s1;
             }
-            n += __shfl_xor(n, 32);
-            if (hf == 0) sm.cnt[wave][row] += n;
+        } else {
+            // the same exponent decides the count: p < small_p  <=>  c*x - LSE2 < log2(small_p);
+            // a key past the causal limit of the row (or past N) is not counted
+            const bool edge = kbase + kWaveKeys > a.Np;  // reaches the window (causal mask) or the end
+            if (!edge) {  // every key of the chunk is visible to every row
+#pragma unroll
+                for (int kb = 0; kb < kKB; ++kb) {
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 16; v += 2) {
+                        const float t0 = x[kb][v] * a.c - lr[v];
+                        const float t1 = x[kb][v + 1] * a.c - lr[v + 1];
+                        s0 += fexp2(t0);
+                        s1 += fexp2(t1);
+                        cn.c[0][v >> 2] += ((uint32_t)(t0 < a.l2tau) << (8 * (v & 3))) +
+                                           ((uint32_t)(t1 < a.l2tau) << (8 * ((v + 1) & 3)));
+                    }
+                    cs[kb] += s0 + s1;
+                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < kKB; ++kb) {
+                    const int j = kbase + kb * 32 + col;
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 16; v += 2) {
+                        const float t0 = x[kb][v] * a.c - lr[v];
+                        const float t1 = x[kb][v + 1] * a.c - lr[v + 1];
+                        s0 += fexp2(t0);
+                        s1 += fexp2(t1);
+                        const int r0 = rb * 32 + tile_row(v, hf), r1 = rb * 32 + tile_row(v + 1, hf);
+                        const bool in0 = r0 < a.R && j <= a.Np + r0 % a.w;
+                        const bool in1 = r1 < a.R && j <= a.Np + r1 % a.w;
+                        cn.c[0][v >> 2] += ((uint32_t)(in0 && t0 < a.l2tau) << (8 * (v & 3))) +
+                                           ((uint32_t)(in1 && t1 < a.l2tau) << (8 * ((v + 1) & 3)));
+                    }
+                    cs[kb] += s0 + s1;
+                }
+            }
+            cn.rotate();
         }
     }
+    if constexpr (ST)
+        for (int rb = a.rbn; rb < RBN; ++rb) cn.rotate();
     const int slab = c.seg / a.spp;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
@@ -354,6 +410,31 @@ __device__ __forceinline__ void pass1_finish(Smem<D, RBN, ST>& sm, const StreamA
     }
 }
 
+// Pass 2 with ST, end of a segment: each field summed over the 32 lanes of its
+// lane half (keys) into the wave's per-row count in LDS, then cleared.
+template <int D, int RBN>
+__device__ __forceinline__ void count_flush(Smem<D, RBN, true>& sm, int wave, int col, int hf, CountState<RBN>& cn) {
+#pragma unroll
+    for (int rb = 0; rb < RBN; ++rb)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t lo = cn.c[rb][w] & 0x00FF00FFu;         // fields of v = 4w and 4w + 2
+            uint32_t hi = (cn.c[rb][w] >> 8) & 0x00FF00FFu;  // fields of v = 4w + 1 and 4w + 3
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                lo += __shfl_xor(lo, off);
+                hi += __shfl_xor(hi, off);
+            }
+            if (col == 0) {
+                sm.cnt[wave][rb * 32 + tile_row(4 * w, hf)] += lo & 0xFFFFu;
+                sm.cnt[wave][rb * 32 + tile_row(4 * w + 1, hf)] += hi & 0xFFFFu;
+                sm.cnt[wave][rb * 32 + tile_row(4 * w + 2, hf)] += lo >> 16;
+                sm.cnt[wave][rb * 32 + tile_row(4 * w + 3, hf)] += hi >> 16;
+            }
+        }
+    cn.reset();
+}
+
 // Pass 2 with ST, end of a segment: the waves' counts of every row.
 template <int D, int RBN>
 __device__ __forceinline__ void pass2_finish(Smem<D, RBN, true>& sm, const StreamArgs& a, int seg, int tid) {
@@ -371,7 +452,8 @@ __device__ __forceinline__ void pass2_finish(Smem<D, RBN, true>& sm, const Strea
 // Returns false once the work-group's sequence ends.
 template <int D, int RBN, int PASS, bool ST>
 __device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, const StreamArgs& a, Cursor& cur, Frag<D>& f,
-                                     Frag<D>& g, int tid, int wave, int col, int hf, RowState<RBN>& rs) {
+                                     Frag<D>& g, int tid, int wave, int col, int hf, RowState<RBN>& rs,
+                                     CountState<RBN>& cn) {
     const Cursor nx = advance(a, cur);
     // Issued on every step (the last one re-reads the current chunk): with a
     // fixed number of loads in flight the wait for `f` leaves `g`'s in flight.
@@ -379,10 +461,13 @@ __device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, const StreamArgs& a, 
     if (PASS == 1)
         pass1_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf, rs);
     else
-        pass2_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf);
+        pass2_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf, cn);
     if (nx.seg != cur.seg) {
         if (PASS == 1) pass1_finish<D, RBN, ST>(sm, a, cur.seg, tid, rs);
-        if constexpr (ST && PASS == 2) pass2_finish<D, RBN>(sm, a, cur.seg, tid);
+        if constexpr (ST && PASS == 2) {
+            count_flush<D, RBN>(sm, wave, col, hf, cn);
+            pass2_finish<D, RBN>(sm, a, cur.seg, tid);
+        }
         if (nx.seg < 0) return false;
         stage<D, RBN, PASS, ST>(sm, a, nx.seg, tid);
     }
@@ -396,7 +481,7 @@ stream_kernel(StreamArgs a) {
     __shared__ __attribute__((aligned(16))) Smem<D, RBN, ST> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps chunk bounds scalar
     const int col = lane & 31;
     const int hf = lane >> 5;
 
@@ -412,12 +497,14 @@ stream_kernel(StreamArgs a) {
     Frag<D> fa, fb;
     RowState<RBN> rs;
     rs.reset();
+    CountState<RBN> cn;
+    cn.reset();
     load_chunk<D>(fa, a, cur, wave, col, hf);
     stage<D, RBN, PASS, ST>(sm, a, cur.seg, tid);
 
     for (;;) {
-        if (!step<D, RBN, PASS, ST>(sm, a, cur, fa, fb, tid, wave, col, hf, rs)) break;
-        if (!step<D, RBN, PASS, ST>(sm, a, cur, fb, fa, tid, wave, col, hf, rs)) break;
+        if (!step<D, RBN, PASS, ST>(sm, a, cur, fa, fb, tid, wave, col, hf, rs, cn)) break;
+        if (!step<D, RBN, PASS, ST>(sm, a, cur, fb, fa, tid, wave, col, hf, rs, cn)) break;
     }
 }
 
@@ -524,7 +611,8 @@ void segments(int64_t keys, int64_t S, int n_wg, int& spp, int& seg_len) {
     const int64_t chunks = (keys + kChunk - 1) / kChunk;
     if (want > chunks) want = chunks;
     if (want < 1) want = 1;
-    const int64_t per = (chunks + want - 1) / want;  // chunks per segment
+    int64_t per = (chunks + want - 1) / want;  // chunks per segment
+    if (per > kMaxSegChunks) per = kMaxSegChunks;
     seg_len = (int)(per * kChunk);
     spp = (int)((keys + seg_len - 1) / seg_len);
     if (spp < 1) spp = 1;
