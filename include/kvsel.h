@@ -258,6 +258,12 @@ kvsel_status_t kvsel_topk_sinks(int32_t batch, int32_t rows, int64_t n_keys, int
  *              ascending.
  * n_merge must not exceed kvsel_csm_candidates(...). head_dim 64 or 128.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ *
+ * kvsel_csm_candidates: host-only; the number of A tokens that have a B
+ * partner (n_merge's upper bound), or -1 for invalid sizes (n_tokens outside
+ * [1, 2^31), chunk odd or outside 2..64, n_sink or n_recent negative or
+ * together above n_tokens). kvsel_csm_workspace_bytes: 0 on invalid
+ * arguments.
  */
 int64_t kvsel_csm_candidates(int64_t n_tokens, int32_t chunk, int32_t n_sink, int32_t n_recent);
 size_t kvsel_csm_workspace_bytes(int32_t n_slabs, int64_t n_tokens, int32_t chunk, int32_t n_sink, int32_t n_recent,

@@ -263,3 +263,38 @@ def test_pivot_layer_rejects(lib):
     assert _pivot(lib, [], [], 0.1, 0.1)[0] == 1
     assert _pivot(lib, [1.0], [0.0], float("nan"), 0.1)[0] == 1
     assert lib.kvsel_pivot_layer(1, None, None, 0.1, 0.1, None) == 1
+
+
+def test_csm_rejects(lib):
+    assert lib.kvsel_csm_candidates(100, 3, 0, 0) == -1       # odd chunk
+    assert lib.kvsel_csm_candidates(100, 66, 0, 0) == -1      # chunk above 64
+    assert lib.kvsel_csm_candidates(100, 8, 60, 50) == -1     # sinks + recent above n
+    assert lib.kvsel_csm_candidates(0, 8, 0, 0) == -1
+    assert lib.kvsel_csm_candidates(100, 8, 2, 2) == 48       # 96 middle tokens: 12 chunks x 4
+    assert lib.kvsel_csm_workspace_bytes(1, 100, 8, 2, 2, 49) == 0  # more merges than candidates
+    need = lib.kvsel_csm_workspace_bytes(2, 100, 8, 2, 2, 10)
+    assert need > 0
+    # the workspace is one byte short in every call, so none can reach a launch
+    ok = [2, 100, 128, 8, 2, 2, 10, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, need - 1, None]
+    assert lib.kvsel_csm(*ok) == 3  # the workspace is checked last, after every argument
+    for i, bad in [(0, 0), (2, 96), (3, 5), (6, 49), (7, None), (8, None), (10, None), (11, None), (12, None),
+                   (7, FAKE + 8)]:
+        args = list(ok)
+        args[i] = bad
+        st = lib.kvsel_csm(*args)
+        assert st == (2 if (i == 2) else 1), (i, bad, st)
+
+
+def test_decode_rejects(lib):
+    need = lib.kvsel_decode_workspace_bytes(2, 8, 2, 128, 1000)
+    assert need > 0
+    assert lib.kvsel_decode_workspace_bytes(2, 18, 2, 128, 1000) == 0  # 9 query heads per KV head
+    assert lib.kvsel_decode_workspace_bytes(2, 8, 3, 128, 1000) == 0   # heads not a multiple
+    # the workspace is one byte short in every call, so none can reach a launch
+    ok = [2, 8, 2, 128, 1000, 0.0, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, None]
+    assert lib.kvsel_decode_attention(*ok) == 3
+    for i, bad, st in [(0, 0, 1), (4, 0, 1), (3, 96, 2), (1, 18, 2), (5, float("nan"), 1), (6, None, 1),
+                       (7, None, 1), (8, None, 1), (10, None, 1), (7, FAKE + 8, 1)]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.kvsel_decode_attention(*args) == st, (i, bad)

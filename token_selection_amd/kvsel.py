@@ -353,6 +353,10 @@ def kvsel_csm(k: torch.Tensor, v: torch.Tensor, degree: Optional[torch.Tensor] =
                                tuple(degree.shape) != lead + (n,)):
         raise ValueError("degree must be a contiguous int32 [..., n] tensor")
     cand = int(lib.kvsel_csm_candidates(n, chunk, n_sink, n_recent))
+    if cand < 0:
+        raise ValueError("invalid CSM sizes (chunk even in 2..64, 0 <= n_sink, n_recent, n_sink + n_recent <= n)")
+    if not (0 <= n_merge <= cand):
+        raise ValueError(f"n_merge must be in [0, {cand}] (A tokens with a partner)")
     n_out = n - n_merge
     dev = k.device
     k_out = torch.empty(lead + (n_out, d), dtype=k.dtype, device=dev)
