@@ -48,6 +48,40 @@ struct DecGeom {
 
 __device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// x moved across lanes by the DPP control CTRL (every lane valid).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row, in every lane of it: pairs, quads
+// (quad_perm), halves (row_half_mirror), the row (row_mirror). VALU only.
+__device__ __forceinline__ float row_sum16(float a) {
+    a += dpp<0xB1>(a);   // quad_perm [1, 0, 3, 2]
+    a += dpp<0x4E>(a);   // quad_perm [2, 3, 0, 1]
+    a += dpp<0x141>(a);  // row_half_mirror
+    a += dpp<0x140>(a);  // row_mirror
+    return a;
+}
+
+// Max / sum over the wave of a value that is uniform within each 16-lane
+// row: the four row values read into scalars (no LDS round trip).
+__device__ __forceinline__ float rows_max4(float x) {
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ float rows_sum4(float x) {
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return (a + b) + (c + d);
+}
+
 // EL consecutive bf16 elements kept as raw 32-bit words until use.
 template <int EL>
 struct Slice {
@@ -79,10 +113,15 @@ __device__ __forceinline__ float elem(const Slice<EL>& s, int e) {
 }
 
 // Waves per SIMD the register state allows without spills (128, 168 or 256
-// registers a wave).
+// registers a wave); also the resident work-groups per CU the host plans for
+// (a work-group has one wave per SIMD).
+__host__ __device__ constexpr int dec_waves(int d, int G) {
+    return d == 128 ? (G <= 2 ? 4 : G <= 5 ? 3 : 2) : (G <= 4 ? 4 : 3);
+}
+
 template <int D, int G>
 constexpr int dec_waves_per_eu() {
-    return D == 128 ? (G <= 2 ? 4 : G <= 4 ? 3 : 2) : (G <= 4 ? 4 : 3);
+    return dec_waves(D, G);
 }
 
 template <int D, int G>
@@ -147,14 +186,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
 #pragma unroll
         for (int t = 0; t < kT; ++t)
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg) {
-                float a = s[t][gg];
-                a += __shfl_xor(a, 1);
-                a += __shfl_xor(a, 2);
-                a += __shfl_xor(a, 4);
-                a += __shfl_xor(a, 8);
-                s[t][gg] = a;
-            }
+            for (int gg = 0; gg < G; ++gg) s[t][gg] = row_sum16(s[t][gg]);
         // --- online softmax: the block's maximum and weight sum over its rows
         float lb[kT];
 #pragma unroll
@@ -170,8 +202,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
                 s[t][gg] = s[t][gg] * g.c + lb[t];
                 bm = fmaxf(bm, s[t][gg]);
             }
-            bm = fmaxf(bm, __shfl_xor(bm, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            bm = rows_max4(bm);
             const float mn = fmaxf(m[gg], bm);
             float ps = 0.f;
 #pragma unroll
@@ -179,8 +210,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
                 s[t][gg] = exp2f(s[t][gg] - mn);
                 ps += s[t][gg];
             }
-            ps += __shfl_xor(ps, 16);
-            ps += __shfl_xor(ps, 32);
+            ps = rows_sum4(ps);
             const float kept = l[gg] * exp2f(m[gg] - mn);  // the old weights on the new reference
             const float ln = kept + ps;
             const float inv = 1.0f / ln;
@@ -274,9 +304,6 @@ __global__ void decode_combine_kernel(DecGeom g, const float* part_m, const floa
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Resident work-groups per CU of decode_kernel<d, G> (a work-group has one
-// wave per SIMD): dec_waves_per_eu on the host.
-int resident_per_cu(int d, int G) { return d == 128 ? (G <= 2 ? 4 : G <= 4 ? 3 : 2) : (G <= 4 ? 4 : 3); }
 
 DecGeom plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, float scale, int n_cu) {
     DecGeom g;
@@ -288,7 +315,7 @@ DecGeom plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t n, float sca
     // one full wave of resident work-groups (a second, partial wave would run
     // at a fraction of the occupancy), each split at least 256 keys
     const int64_t units = (int64_t)B * Hkv;
-    const int64_t target = (int64_t)n_cu * resident_per_cu(d, g.G);
+    const int64_t target = (int64_t)n_cu * dec_waves(d, g.G);
     int64_t s = (target + units - 1) / units;
     const int64_t max_s = (n + 255) / 256;
     if (s > max_s) s = max_s;
