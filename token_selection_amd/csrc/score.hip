@@ -215,17 +215,36 @@ __global__ __launch_bounds__(256) void lse_partial_kernel(ScoreGeom g) {
 
 // Merge the chunk partials of each row into its LSE (log2 domain); padded
 // rows get +inf so that pass 2 gives them probability 0.
+// A block takes kCombRows rows; each row's chunks are spread over
+// kCombSubs threads (thread t: row t % kCombRows, every kCombSubs-th chunk
+// from t / kCombRows on, so a wave reads consecutive rows of a chunk), whose
+// running (max, sum) states then merge through LDS.
+constexpr int kCombRows = 16;
+constexpr int kCombSubs = 256 / kCombRows;
+
 __global__ __launch_bounds__(256) void lse_combine_kernel(ScoreGeom g) {
+    __shared__ float2 red[kCombSubs][kCombRows];
     const int s = blockIdx.y;
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= g.Rpad) return;
-    const float2* p = g.part + (int64_t)s * g.n_chunks1 * g.Rpad + r;
-    float M = -INFINITY;
-    for (int c = 0; c < g.n_chunks1; ++c) M = fmaxf(M, p[(int64_t)c * g.Rpad].x);
-    float Z = 0.f;
-    for (int c = 0; c < g.n_chunks1; ++c) {
-        const float2 v = p[(int64_t)c * g.Rpad];
-        Z += v.y * exp2f(v.x - M);
+    const int rl = threadIdx.x % kCombRows, sub = threadIdx.x / kCombRows;
+    const int r = blockIdx.x * kCombRows + rl;
+    float M = kNegBig, Z = 0.f;
+    if (r < g.Rpad) {
+        const float2* p = g.part + (int64_t)s * g.n_chunks1 * g.Rpad + r;
+        for (int c = sub; c < g.n_chunks1; c += kCombSubs) {
+            const float2 v = p[(int64_t)c * g.Rpad];
+            const float mn = fmaxf(M, v.x);
+            Z = Z * exp2f(M - mn) + v.y * exp2f(v.x - mn);
+            M = mn;
+        }
+    }
+    red[sub][rl] = make_float2(M, Z);
+    __syncthreads();
+    if (sub != 0 || r >= g.Rpad) return;
+    for (int s2 = 1; s2 < kCombSubs; ++s2) {
+        const float2 o = red[s2][rl];
+        const float mn = fmaxf(M, o.x);
+        Z = Z * exp2f(M - mn) + o.y * exp2f(o.x - mn);
+        M = mn;
     }
     if (r < g.R) {
         const float l2 = M + log2f(Z);
@@ -401,7 +420,7 @@ void launch_passes(const ScoreGeom& g, hipStream_t st) {
                            g.S, g.Rpad, g.R, g.w, g.B, g.Hq, g.Hkv, g.G);
     } else {
         hipLaunchKernelGGL((lse_partial_kernel<T, D, RB>), dim3(g.n_chunks1, g.S), dim3(256), 0, st, g);
-        hipLaunchKernelGGL(lse_combine_kernel, dim3((g.Rpad + 255) / 256, g.S), dim3(256), 0, st, g);
+        hipLaunchKernelGGL(lse_combine_kernel, dim3((g.Rpad + kCombRows - 1) / kCombRows, g.S), dim3(256), 0, st, g);
     }
     if (g.Np > 0)
         hipLaunchKernelGGL((raw_score_kernel<T, D, RB>), dim3(g.n_chunks2, g.S), dim3(256), 0, st, g);

@@ -508,16 +508,37 @@ stream_kernel(StreamArgs a) {
     }
 }
 
+// The merge kernels below run 256 threads per slab (R <= 256 rows): thread
+// t takes row t % RQ and every (256/RQ)-th segment from t / RQ on, where RQ
+// is the power of two at or above R, so a wave reads consecutive rows of a
+// segment and short row counts still spread a long segment list over many
+// threads; the per-thread states then merge through LDS.
+__device__ __forceinline__ int row_span(int R) {
+    int q = 1;
+    while (q < R) q <<= 1;
+    return q;
+}
+
 // Row LSE2 of every slab from its segments' partials; padded rows are left
 // alone (pass 2 stages +inf for them).
-__global__ void stream_merge_kernel(const float2* part, int spp, int rp, int R, int w, int B, int Hq, int Hkv,
-                                    int G, float* lse2, float* lse_out) {
+__global__ __launch_bounds__(256) void stream_merge_kernel(const float2* part, int spp, int rp, int R, int w, int B,
+                                                           int Hq, int Hkv, int G, float* lse2, float* lse_out) {
+    __shared__ float2 red[256];
     const int slab = blockIdx.x;
-    for (int row = threadIdx.x; row < R; row += blockDim.x) {
-        float M = kNegBig, Z = 0.f;
-        for (int p = 0; p < spp; ++p) {
+    const int rq = row_span(R), nsub = 256 / rq;
+    const int row = threadIdx.x % rq, sub = threadIdx.x / rq;
+    float M = kNegBig, Z = 0.f;
+    if (row < R)
+        for (int p = sub; p < spp; p += nsub) {
             const float2 v = part[((int64_t)slab * spp + p) * rp + row];
             merge(M, Z, v.x, v.y);
+        }
+    red[threadIdx.x] = make_float2(M, Z);
+    __syncthreads();
+    if (sub == 0 && row < R) {
+        for (int s2 = 1; s2 < nsub; ++s2) {
+            const float2 o = red[s2 * rq + row];
+            merge(M, Z, o.x, o.y);
         }
         const float l2 = M + log2f(Z);
         lse2[(int64_t)slab * rp + row] = l2;
@@ -542,16 +563,26 @@ __device__ __forceinline__ int64_t row_out(int slab, int row, int w, int B, int 
 
 // ST merge: row LSE2 as above, plus the row's entropy
 // -sum p ln p = ln2 * (LSE2 - c * sum p*x) and sum p^2 = q / z^2.
-__global__ void stream_merge_st_kernel(const float4* part, int spp, int rp, int R, int w, int B, int Hq, int Hkv,
-                                       int G, float c, float* lse2, float* lse_out, float* entropy,
-                                       float* sum_p2) {
+__global__ __launch_bounds__(256) void stream_merge_st_kernel(const float4* part, int spp, int rp, int R, int w,
+                                                              int B, int Hq, int Hkv, int G, float c, float* lse2,
+                                                              float* lse_out, float* entropy, float* sum_p2) {
+    __shared__ float4 red[256];
     const int slab = blockIdx.x;
-    for (int row = threadIdx.x; row < R; row += blockDim.x) {
-        float M = kNegBig, Z = 0.f;
-        Moments mo{0.f, 0.f};
-        for (int p = 0; p < spp; ++p) {
+    const int rq = row_span(R), nsub = 256 / rq;
+    const int row = threadIdx.x % rq, sub = threadIdx.x / rq;
+    float M = kNegBig, Z = 0.f;
+    Moments mo{0.f, 0.f};
+    if (row < R)
+        for (int p = sub; p < spp; p += nsub) {
             const float4 v = part[((int64_t)slab * spp + p) * rp + row];
             merge_st(M, Z, mo, v.x, v.y, Moments{v.z, v.w});
+        }
+    red[threadIdx.x] = make_float4(M, Z, mo.s, mo.q);
+    __syncthreads();
+    if (sub == 0 && row < R) {
+        for (int s2 = 1; s2 < nsub; ++s2) {
+            const float4 o = red[s2 * rq + row];
+            merge_st(M, Z, mo, o.x, o.y, Moments{o.z, o.w});
         }
         const float l2 = M + log2f(Z);
         lse2[(int64_t)slab * rp + row] = l2;
@@ -564,12 +595,19 @@ __global__ void stream_merge_st_kernel(const float4* part, int spp, int rp, int 
 }
 
 // ST: every row's count of keys below the threshold, summed over segments.
-__global__ void stream_count_kernel(const uint32_t* cnt_part, int spp, int rp, int R, int w, int B, int Hq, int Hkv,
-                                    int G, int32_t* n_below) {
+__global__ __launch_bounds__(256) void stream_count_kernel(const uint32_t* cnt_part, int spp, int rp, int R, int w,
+                                                           int B, int Hq, int Hkv, int G, int32_t* n_below) {
+    __shared__ uint32_t red[256];
     const int slab = blockIdx.x;
-    for (int row = threadIdx.x; row < R; row += blockDim.x) {
-        uint32_t n = 0;
-        for (int p = 0; p < spp; ++p) n += cnt_part[((int64_t)slab * spp + p) * rp + row];
+    const int rq = row_span(R), nsub = 256 / rq;
+    const int row = threadIdx.x % rq, sub = threadIdx.x / rq;
+    uint32_t n = 0;
+    if (row < R)
+        for (int p = sub; p < spp; p += nsub) n += cnt_part[((int64_t)slab * spp + p) * rp + row];
+    red[threadIdx.x] = n;
+    __syncthreads();
+    if (sub == 0 && row < R) {
+        for (int s2 = 1; s2 < nsub; ++s2) n += red[s2 * rq + row];
         n_below[row_out(slab, row, w, B, Hq, Hkv, G)] = (int32_t)n;
     }
 }
