@@ -99,8 +99,10 @@ size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc);
  *         window row.
  * workspace  device, >= kvsel_score_workspace_bytes(desc) bytes, 256-byte
  *         aligned; its content is scratch between calls.
- * Paths: bf16 with head_dim 64/128 and G*w <= 256 streams K in two passes;
- * other shapes take a general two-pass path. The environment variable
+ * Paths: bf16 with head_dim 64/128 and w <= 256 streams K in two passes
+ * (when G*w > 256 the group's query heads are streamed in row groups of at
+ * most 256 rows, each reading the keys); other shapes take a general
+ * two-pass path. The environment variable
  * KVSEL_SCORE_PATH=resident (register-resident, single K read) or =general
  * forces another path where it applies; every path computes the same result
  * to the stated tolerance.
@@ -142,7 +144,7 @@ kvsel_status_t kvsel_score_lse(const kvsel_score_desc_t* desc, const void* q_win
  *          p_j < small_p (decided in fp32 on the exponent: c*x - LSE2 <
  *          log2(small_p), c = scale*log2(e); keys within rounding of the
  *          threshold may fall either way).
- * Only the streaming path computes them: bf16, head_dim 64/128, G*w <= 256;
+ * Only the streaming path computes them: bf16, head_dim 64/128, w <= 256;
  * other shapes return UNSUPPORTED. Both passes read every key.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */

@@ -80,7 +80,7 @@ def check_stats(wl, inp, gpu, small_p, heads=None, ref_stats=None):
     return ref
 
 
-# (L, B, Hq, Hkv, d, N, w, pool) -- bf16, G*w <= 256
+# (L, B, Hq, Hkv, d, N, w, pool) -- bf16
 SHAPES = [
     (1, 1, 4, 1, 128, 3001, 5, 7),      # ragged last chunk, G = 4
     (2, 2, 6, 2, 64, 2500, 7, 3),       # d = 64, G = 3, 2 layers, 2 sequences
@@ -89,6 +89,7 @@ SHAPES = [
     (1, 1, 8, 2, 128, 777, 64, 5),      # 256 rows
     (1, 2, 4, 2, 128, 40, 40, 7),       # w = N: no prefix, only window keys
     (1, 1, 4, 2, 128, 41, 40, 7),       # one prefix key
+    (2, 1, 28, 4, 64, 2100, 64, 7),     # 448 rows: row groups of 4 and 3 heads, 2 layers
 ]
 
 

@@ -95,11 +95,26 @@ struct Plan {
     int RB;
     ScoreWs gen;               // general two-pass layout (any dtype)
     kvsel::StreamPlan stream;  // streaming bf16 layout (stream.ok when eligible)
+    int T, Gs;                 // streaming row groups: T groups of at most Gs query heads per KV head
     kvsel::KresPlan kres;      // register-resident bf16 layout (kres.ok when eligible)
     size_t stream_total, kres_total, total;
 };
 
-size_t raw_bytes(const ScoreGeom& g) { return ((size_t)g.S * g.Np * sizeof(float) + 255) & ~(size_t)255; }
+size_t raw_bytes(int64_t S, int64_t Np) { return ((size_t)S * Np * sizeof(float) + 255) & ~(size_t)255; }
+size_t raw_bytes(const ScoreGeom& g) { return raw_bytes(g.S, g.Np); }
+
+// The streaming kernels hold at most 256 window rows per slab. Past that, a
+// KV head's query heads split into T row groups of at most Gs heads each
+// (Gs*w <= 256, sizes balanced), each streamed as a slab of its own over the
+// same keys; their raw scores add up like extra layers.
+void row_groups(const ScoreGeom& g, int& T, int& Gs) {
+    T = 1;
+    Gs = g.G;
+    if (g.R <= 256 || g.w > 256) return;
+    Gs = 256 / g.w;
+    T = (g.G + Gs - 1) / Gs;
+    Gs = (g.G + T - 1) / T;
+}
 
 void make_plan(const kvsel_score_desc_t* d, Plan& p) {
     make_geom(d, p.g, p.RB);
@@ -107,8 +122,12 @@ void make_plan(const kvsel_score_desc_t* d, Plan& p) {
     p.total = p.gen.total;
     const int n_cu = device_cu_count();
     p.stream_total = p.kres_total = 0;
-    if (kvsel::stream_plan(d->dtype, d->head_dim, p.g.R, p.g.N, p.g.Np, p.g.S, n_cu, p.stream)) {
-        p.stream_total = p.stream.raw_off + raw_bytes(p.g);
+    row_groups(p.g, p.T, p.Gs);
+    const int64_t S_groups = (int64_t)p.g.S * p.T;
+    p.stream.ok = false;
+    if (S_groups <= 65535 &&
+        kvsel::stream_plan(d->dtype, d->head_dim, p.Gs * p.g.w, p.g.N, p.g.Np, S_groups, n_cu, p.stream)) {
+        p.stream_total = p.stream.raw_off + raw_bytes(S_groups, p.g.Np);
         if (p.stream_total > p.total) p.total = p.stream_total;
     }
     if (kvsel::kres_plan(d->dtype, d->head_dim, p.g.R, p.g.N, p.g.S, n_cu, p.kres)) {
@@ -159,6 +178,7 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
     g.lse_out = lse_out;
     g.lse_in = lse_in;
     float* raw = nullptr;
+    int raw_layers = g.L;  // slices of raw that the pool sums (layers, times row groups)
     bool done = false;
     if (stats && !p.stream.ok) return KVSEL_ERR_UNSUPPORTED;  // the statistics ride on the streaming passes
     Path path = stats ? Path::Stream : choose_path(p);
@@ -176,11 +196,13 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         a.Hkv = g.Hkv;
         a.G = g.G;
         a.w = g.w;
-        a.R = g.R;
-        a.rbn = p.stream.rbn;
+        a.T = p.T;
+        a.Gs = p.Gs;
+        a.S0 = g.S;
+        a.R = p.Gs * g.w;
         a.N = (int32_t)g.N;
         a.Np = (int32_t)g.Np;
-        a.S = g.S;
+        a.S = g.S * p.T;
         a.c = g.c;
         a.invG = g.invG;
         a.part = reinterpret_cast<float2*>(ws + p.stream.part_off);
@@ -194,14 +216,24 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
                 hipSuccess)
                 return KVSEL_ERR_HIP;
         } else if (lse_in) {
-            if (kvsel::launch_lse_from_input(lse_in, a.lse2, g.S, p.stream.rp, g.R, g.w, g.B, g.Hq, g.Hkv, g.G, hs) !=
-                    hipSuccess ||
+            if (kvsel::launch_lse_from_input(lse_in, a.lse2, a.S, p.stream.rp, a.R, g.w, g.B, g.Hq, g.Hkv, g.G, g.S,
+                                             p.Gs, hs) != hipSuccess ||
                 kvsel::launch_stream_pass2(p.stream, a, hs) != hipSuccess)
                 return KVSEL_ERR_HIP;
         } else if (kvsel::launch_stream(p.stream, a, lse_out, hs) != hipSuccess) {
             return KVSEL_ERR_HIP;
         }
         raw = a.raw;
+        raw_layers = g.L * p.T;
+        if (p.T > 1 && desc->pool_type == KVSEL_POOL_MAX && g.Np > 0) {
+            // the max pool is not linear: add the row groups into the first
+            // group's slices first, then pool layer by layer
+            for (int t = 1; t < p.T; ++t)
+                if (kvsel::launch_accumulate(1, g.S, g.Np, raw + (int64_t)t * g.S * g.Np, raw, KVSEL_ACC_ADD, hs) !=
+                    hipSuccess)
+                    return KVSEL_ERR_HIP;
+            raw_layers = g.L;
+        }
         done = true;
     }
     if (path == Path::Resident) {
@@ -252,7 +284,7 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         if (e != hipSuccess) return KVSEL_ERR_HIP;
         raw = g.raw;
     }
-    return from_hip(kvsel::launch_pool(raw, scores, g.L, (int64_t)g.B * g.Hkv, g.Np, desc->pool_kernel,
+    return from_hip(kvsel::launch_pool(raw, scores, raw_layers, (int64_t)g.B * g.Hkv, g.Np, desc->pool_kernel,
                                        desc->pool_type, accumulate ? 1 : 0, hs));
 }
 

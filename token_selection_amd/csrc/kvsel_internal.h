@@ -45,8 +45,10 @@ hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int 
 
 // Row LSE2 [S][stride] (log2 domain, +inf past R) from a handed-in natural-log
 // LSE [L][B][Hq][w].
+// Slabs are [T][S0] row groups of Gs heads each (T = 1, Gs = G without
+// groups); R is the row count of a full group.
 hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B, int Hq,
-                                 int Hkv, int G, hipStream_t stream);
+                                 int Hkv, int G, int S0, int Gs, hipStream_t stream);
 
 // Pool (KVSEL_POOL_AVG or _MAX) of raw [L][B*Hkv][Np], summed over layers,
 // written or added to scores.
@@ -94,8 +96,13 @@ struct StreamArgs {
     const uint16_t* k;
     int64_t qs[4];
     int64_t ks[4];
-    int32_t B, Hq, Hkv, G, w, R, rbn;
+    int32_t B, Hq, Hkv, G, w, R;
     int32_t N, Np, S;
+    // Row groups: when the G*w rows of a KV head exceed the kernels' 256,
+    // its query heads split into T groups of Gs heads (the last may hold
+    // fewer), each a slab of its own. Slabs are [T][S0] with S0 = L*B*Hkv;
+    // R = Gs*w is the row count of a full group.
+    int32_t T, Gs, S0;
     int32_t spp;      // segments per slab (set per pass)
     int32_t seg_len;  // keys per segment, a multiple of the 256-key chunk
     int32_t n_range;  // keys the pass covers: N (pass 1, and pass 2 with statistics) or Np (pass 2)

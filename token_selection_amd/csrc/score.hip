@@ -397,16 +397,18 @@ __global__ __launch_bounds__(256) void pool_max_acc_kernel(const float* __restri
 // already has it): lse2[s][r] = LSE[l][b][g*G + r/w][r%w] * log2(e) for r < R,
 // +inf (probability 0) on padded rows.
 __global__ void lse_from_input_kernel(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B,
-                                      int Hq, int Hkv, int G) {
+                                      int Hq, int Hkv, int G, int S0, int Gs) {
     const int s = blockIdx.y;
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= S || r >= stride) return;
+    const int t = s / S0, s0 = s - t * S0;  // row group, (layer, b, kv head) slab
+    const int rows = min(Gs, G - t * Gs) * w;
     float v = INFINITY;
-    if (r < R) {
-        const int kvh = s % Hkv;
-        const int b = (s / Hkv) % B;
-        const int l = s / (Hkv * B);
-        const int h = kvh * G + r / w;
+    if (r < rows && r < R) {
+        const int kvh = s0 % Hkv;
+        const int b = (s0 / Hkv) % B;
+        const int l = s0 / (Hkv * B);
+        const int h = kvh * G + t * Gs + r / w;
         const int i = r % w;
         v = lse_in[(((int64_t)l * B + b) * Hq + h) * w + i] * 1.44269504088896340736f;
     }
@@ -417,7 +419,7 @@ template <typename T, int D, int RB>
 void launch_passes(const ScoreGeom& g, hipStream_t st) {
     if (g.lse_in) {
         hipLaunchKernelGGL(lse_from_input_kernel, dim3((g.Rpad + 255) / 256, g.S), dim3(256), 0, st, g.lse_in, g.lse2,
-                           g.S, g.Rpad, g.R, g.w, g.B, g.Hq, g.Hkv, g.G);
+                           g.S, g.Rpad, g.R, g.w, g.B, g.Hq, g.Hkv, g.G, g.S, g.G);
     } else {
         hipLaunchKernelGGL((lse_partial_kernel<T, D, RB>), dim3(g.n_chunks1, g.S), dim3(256), 0, st, g);
         hipLaunchKernelGGL(lse_combine_kernel, dim3((g.Rpad + kCombRows - 1) / kCombRows, g.S), dim3(256), 0, st, g);
@@ -487,10 +489,10 @@ hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int 
 }
 
 hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B, int Hq,
-                                 int Hkv, int G, hipStream_t st) {
-    if (S < 1 || S > 65535 || stride < 1) return hipErrorInvalidValue;
+                                 int Hkv, int G, int S0, int Gs, hipStream_t st) {
+    if (S < 1 || S > 65535 || stride < 1 || S0 < 1 || Gs < 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(lse_from_input_kernel, dim3((unsigned)((stride + 255) / 256), (unsigned)S), dim3(256), 0, st,
-                       lse_in, lse2, S, stride, R, w, B, Hq, Hkv, G);
+                       lse_in, lse2, S, stride, R, w, B, Hq, Hkv, G, S0, Gs);
     return hipGetLastError();
 }
 

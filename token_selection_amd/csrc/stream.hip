@@ -18,6 +18,10 @@
 // has decides (c*x - LSE2 < log2 threshold), into packed per-lane counters
 // that are summed over the lanes once per segment.
 //
+// A slab holds at most 256 window rows: when a KV head's G*w rows exceed
+// that, its query heads split into row groups, each a slab of its own over
+// the same keys (StreamArgs::T, Gs, S0).
+//
 // No work-group waits for another: every slab is cut into segments of whole
 // 256-key chunks, work-group g takes segments g, g + grid, ..., and while it
 // computes one chunk the loads of its next chunk are in flight into a second
@@ -129,11 +133,19 @@ __device__ __forceinline__ Cursor advance(const StreamArgs& a, Cursor c) {
     return Cursor{-1, 0, 0};
 }
 
+// Slabs are [T][S0]: row group t = slab / S0 of the (layer, b, KV head)
+// slab s0 = slab % S0 (s0 = (l*B + b)*Hkv + g) holds query heads
+// g*G + t*Gs + (0 .. slab_rows/w - 1).
 __device__ __forceinline__ const uint16_t* slab_keys(const StreamArgs& a, int slab) {
-    const int g = slab % a.Hkv;
-    const int b = (slab / a.Hkv) % a.B;
-    const int l = slab / (a.Hkv * a.B);
+    const int s0 = slab % a.S0;
+    const int g = s0 % a.Hkv;
+    const int b = (s0 / a.Hkv) % a.B;
+    const int l = s0 / (a.Hkv * a.B);
     return a.k + l * a.ks[0] + b * a.ks[1] + g * a.ks[2];
+}
+
+__device__ __forceinline__ int slab_rows(const StreamArgs& a, int slab) {
+    return min(a.Gs, a.G - slab / a.S0 * a.Gs) * a.w;
 }
 
 // This wave's 64 keys of a chunk as operand fragments: lane (col, hf) reads
@@ -174,9 +186,12 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
     constexpr int CPK = D / 8;  // 16-byte chunks per row
     constexpr int QPER = (RP * CPK + 255) / 256;
     const int slab = seg / a.spp;
-    const int g = slab % a.Hkv;
-    const int b = (slab / a.Hkv) % a.B;
-    const int l = slab / (a.Hkv * a.B);
+    const int s0 = slab % a.S0;
+    const int g = s0 % a.Hkv;
+    const int b = (s0 / a.Hkv) % a.B;
+    const int l = s0 / (a.Hkv * a.B);
+    const int h0 = g * a.G + slab / a.S0 * a.Gs;  // the row group's first query head
+    const int rows = slab_rows(a, slab);
     const uint16_t* qbase = a.q + l * a.qs[0] + b * a.qs[1];
     __syncthreads();  // every wave is done with the previous segment's rows
     uint4 qv[QPER];
@@ -186,8 +201,8 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
         const int row = idx / CPK;
         const int ch = idx - row * CPK;
         qv[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (row < a.R) {
-            const int h = g * a.G + row / a.w;
+        if (row < rows) {
+            const int h = h0 + row / a.w;
             const int i = row % a.w;
             qv[u] = *reinterpret_cast<const uint4*>(qbase + h * a.qs[2] + i * a.qs[3] + ch * 8);
         }
@@ -200,7 +215,7 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
         }
     } else {
         for (int row = tid; row < RP; row += 256) {
-            const float l2 = row < a.R ? a.lse2[(int64_t)slab * RP + row] : INFINITY;
+            const float l2 = row < rows ? a.lse2[(int64_t)slab * RP + row] : INFINITY;
             sm.lse[row] = l2;
 
         }
@@ -227,9 +242,11 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
     const int kbase = c.first + wave * kWaveKeys;
     if (kbase >= a.N) return;  // the chunk ends before this wave's keys
     const bool edge = kbase + kWaveKeys > a.Np;  // reaches the window (causal mask) or the end
+    const int rows = slab_rows(a, c.seg / a.spp);
+    const int rbn = (rows + 31) >> 5;  // row blocks holding this slab's rows
     if constexpr (!ST) {
 #pragma unroll 1
-        for (int rb = 0; rb < a.rbn; ++rb) {
+        for (int rb = 0; rb < rbn; ++rb) {
             bf16x8 qf[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
@@ -238,7 +255,7 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
             float m, z;
             if (edge) {
                 const int row = rb * 32 + col;
-                const int lim = row < a.R ? a.Np + row % a.w : -1;
+                const int lim = row < rows ? a.Np + row % a.w : -1;
                 z = pass1_max<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m);
             } else {
                 z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
@@ -247,11 +264,11 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
             merge(rs.m[0], rs.z[0], m, z);
             rs.rotate();
         }
-        for (int rb = a.rbn; rb < RBN; ++rb) rs.rotate();
+        for (int rb = rbn; rb < RBN; ++rb) rs.rotate();
         return;
     }
 #pragma unroll 1
-    for (int rb = 0; rb < a.rbn; ++rb) {
+    for (int rb = 0; rb < rbn; ++rb) {
         bf16x8 qf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -262,7 +279,7 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
             Moments mo;
             if (edge) {
                 const int row = rb * 32 + col;
-                const int lim = row < a.R ? a.Np + row % a.w : -1;
+                const int lim = row < rows ? a.Np + row % a.w : -1;
                 z = pass1_max_st<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m, mo);
             } else {
                 z = pass1_fast_st<D, kKB>(f.v, qf, a.c, m, mo);
@@ -288,11 +305,14 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
     constexpr int QST = D + 8;
     const int kbase = c.first + wave * kWaveKeys;
     if (kbase >= a.n_range) return;  // no keys of this pass in this wave's range
+    const int slab = c.seg / a.spp;
+    const int rows = slab_rows(a, slab);
+    const int rbn = (rows + 31) >> 5;  // row blocks holding this slab's rows
     float cs[kKB];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) cs[kb] = 0.f;
 #pragma unroll 1
-    for (int rb = 0; rb < a.rbn; ++rb) {
+    for (int rb = 0; rb < rbn; ++rb) {
         bf16x8 qf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -352,8 +372,8 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
                         s0 += fexp2(t0);
                         s1 += fexp2(t1);
                         const int r0 = rb * 32 + tile_row(v, hf), r1 = rb * 32 + tile_row(v + 1, hf);
-                        const bool in0 = r0 < a.R && j <= a.Np + r0 % a.w;
-                        const bool in1 = r1 < a.R && j <= a.Np + r1 % a.w;
+                        const bool in0 = r0 < rows && j <= a.Np + r0 % a.w;
+                        const bool in1 = r1 < rows && j <= a.Np + r1 % a.w;
                         cn.c[0][v >> 2] += ((uint32_t)(in0 && t0 < a.l2tau) << (8 * (v & 3))) +
                                            ((uint32_t)(in1 && t1 < a.l2tau) << (8 * ((v + 1) & 3)));
                     }
@@ -364,8 +384,7 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
         }
     }
     if constexpr (ST)
-        for (int rb = a.rbn; rb < RBN; ++rb) cn.rotate();
-    const int slab = c.seg / a.spp;
+        for (int rb = rbn; rb < RBN; ++rb) cn.rotate();
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
         const float val = cs[kb] + __shfl_xor(cs[kb], 32);
@@ -508,27 +527,53 @@ stream_kernel(StreamArgs a) {
     }
 }
 
-// The merge kernels below run 256 threads per slab (R <= 256 rows): thread
-// t takes row t % RQ and every (256/RQ)-th segment from t / RQ on, where RQ
-// is the power of two at or above R, so a wave reads consecutive rows of a
-// segment and short row counts still spread a long segment list over many
-// threads; the per-thread states then merge through LDS.
+// Rows of a slab and where its row statistics go: slab = t*S0 + s0 with
+// s0 = (l*B + b)*Hkv + g, row r -> query head g*G + t*Gs + r/w, window
+// index r%w, output index ((l*B + b)*Hq + head)*w + r%w.
+struct RowMap {
+    int w, B, Hq, Hkv, G, S0, Gs;
+    __device__ int rows(int slab) const { return min(Gs, G - slab / S0 * Gs) * w; }
+    __device__ int64_t out(int slab, int row) const {
+        const int s0 = slab % S0;
+        const int g = s0 % Hkv;
+        const int b = (s0 / Hkv) % B;
+        const int l = s0 / (Hkv * B);
+        const int h = g * G + slab / S0 * Gs + row / w;
+        return (((int64_t)l * B + b) * Hq + h) * w + row % w;
+    }
+};
+
+RowMap row_map(const StreamArgs& a) { return RowMap{a.w, a.B, a.Hq, a.Hkv, a.G, a.S0, a.Gs}; }
+
+// The merge kernels below take blocks of 256 threads over RQ rows of a slab
+// each (grid: slabs x row tiles): RQ is the power of two at or above the
+// slab's row count, at most 32, and thread t takes row t % RQ of the tile and
+// every (256/RQ)-th segment from t / RQ on. A wave reads consecutive rows of
+// a segment, a long segment list is spread over at least 8 threads per row,
+// and the per-thread states then merge through LDS.
+constexpr int kMergeRows = 32;
+
 __device__ __forceinline__ int row_span(int R) {
     int q = 1;
-    while (q < R) q <<= 1;
+    while (q < R && q < kMergeRows) q <<= 1;
     return q;
 }
 
+dim3 merge_grid(const StreamArgs& a) { return dim3((unsigned)a.S, (unsigned)((a.R + kMergeRows - 1) / kMergeRows)); }
+
 // Row LSE2 of every slab from its segments' partials; padded rows are left
 // alone (pass 2 stages +inf for them).
-__global__ __launch_bounds__(256) void stream_merge_kernel(const float2* part, int spp, int rp, int R, int w, int B,
-                                                           int Hq, int Hkv, int G, float* lse2, float* lse_out) {
+__global__ __launch_bounds__(256) void stream_merge_kernel(const float2* part, int spp, int rp, RowMap m, float* lse2,
+                                                           float* lse_out) {
     __shared__ float2 red[256];
     const int slab = blockIdx.x;
+    const int R = m.rows(slab);
     const int rq = row_span(R), nsub = 256 / rq;
-    const int row = threadIdx.x % rq, sub = threadIdx.x / rq;
+    if ((int)blockIdx.y * rq >= R) return;  // the whole tile is past this slab's rows
+    const int row = blockIdx.y * rq + threadIdx.x % rq, sub = threadIdx.x / rq;
     float M = kNegBig, Z = 0.f;
     if (row < R)
+#pragma unroll 4
         for (int p = sub; p < spp; p += nsub) {
             const float2 v = part[((int64_t)slab * spp + p) * rp + row];
             merge(M, Z, v.x, v.y);
@@ -537,42 +582,30 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const float2* part, i
     __syncthreads();
     if (sub == 0 && row < R) {
         for (int s2 = 1; s2 < nsub; ++s2) {
-            const float2 o = red[s2 * rq + row];
+            const float2 o = red[s2 * rq + threadIdx.x % rq];
             merge(M, Z, o.x, o.y);
         }
         const float l2 = M + log2f(Z);
         lse2[(int64_t)slab * rp + row] = l2;
-        if (lse_out) {
-            const int g = slab % Hkv;
-            const int b = (slab / Hkv) % B;
-            const int l = slab / (Hkv * B);
-            const int h = g * G + row / w;
-            const int i = row % w;
-            lse_out[(((int64_t)l * B + b) * Hq + h) * w + i] = l2 * 0.69314718055994530942f;
-        }
+        if (lse_out) lse_out[m.out(slab, row)] = l2 * 0.69314718055994530942f;
     }
-}
-
-// Output index of slab row `row`: (layer, b, head g*G + row / w, row % w).
-__device__ __forceinline__ int64_t row_out(int slab, int row, int w, int B, int Hq, int Hkv, int G) {
-    const int g = slab % Hkv;
-    const int b = (slab / Hkv) % B;
-    const int l = slab / (Hkv * B);
-    return (((int64_t)l * B + b) * Hq + g * G + row / w) * w + row % w;
 }
 
 // ST merge: row LSE2 as above, plus the row's entropy
 // -sum p ln p = ln2 * (LSE2 - c * sum p*x) and sum p^2 = q / z^2.
-__global__ __launch_bounds__(256) void stream_merge_st_kernel(const float4* part, int spp, int rp, int R, int w,
-                                                              int B, int Hq, int Hkv, int G, float c, float* lse2,
-                                                              float* lse_out, float* entropy, float* sum_p2) {
+__global__ __launch_bounds__(256) void stream_merge_st_kernel(const float4* part, int spp, int rp, RowMap m, float c,
+                                                              float* lse2, float* lse_out, float* entropy,
+                                                              float* sum_p2) {
     __shared__ float4 red[256];
     const int slab = blockIdx.x;
+    const int R = m.rows(slab);
     const int rq = row_span(R), nsub = 256 / rq;
-    const int row = threadIdx.x % rq, sub = threadIdx.x / rq;
+    if ((int)blockIdx.y * rq >= R) return;  // the whole tile is past this slab's rows
+    const int row = blockIdx.y * rq + threadIdx.x % rq, sub = threadIdx.x / rq;
     float M = kNegBig, Z = 0.f;
     Moments mo{0.f, 0.f};
     if (row < R)
+#pragma unroll 4
         for (int p = sub; p < spp; p += nsub) {
             const float4 v = part[((int64_t)slab * spp + p) * rp + row];
             merge_st(M, Z, mo, v.x, v.y, Moments{v.z, v.w});
@@ -581,12 +614,12 @@ __global__ __launch_bounds__(256) void stream_merge_st_kernel(const float4* part
     __syncthreads();
     if (sub == 0 && row < R) {
         for (int s2 = 1; s2 < nsub; ++s2) {
-            const float4 o = red[s2 * rq + row];
+            const float4 o = red[s2 * rq + threadIdx.x % rq];
             merge_st(M, Z, mo, o.x, o.y, Moments{o.z, o.w});
         }
         const float l2 = M + log2f(Z);
         lse2[(int64_t)slab * rp + row] = l2;
-        const int64_t o = row_out(slab, row, w, B, Hq, Hkv, G);
+        const int64_t o = m.out(slab, row);
         constexpr float kLn2 = 0.69314718055994530942f;
         if (lse_out) lse_out[o] = l2 * kLn2;
         entropy[o] = kLn2 * (l2 - c * (mo.s / Z));
@@ -595,20 +628,22 @@ __global__ __launch_bounds__(256) void stream_merge_st_kernel(const float4* part
 }
 
 // ST: every row's count of keys below the threshold, summed over segments.
-__global__ __launch_bounds__(256) void stream_count_kernel(const uint32_t* cnt_part, int spp, int rp, int R, int w,
-                                                           int B, int Hq, int Hkv, int G, int32_t* n_below) {
+__global__ __launch_bounds__(256) void stream_count_kernel(const uint32_t* cnt_part, int spp, int rp, RowMap m,
+                                                           int32_t* n_below) {
     __shared__ uint32_t red[256];
     const int slab = blockIdx.x;
+    const int R = m.rows(slab);
     const int rq = row_span(R), nsub = 256 / rq;
-    const int row = threadIdx.x % rq, sub = threadIdx.x / rq;
+    if ((int)blockIdx.y * rq >= R) return;  // the whole tile is past this slab's rows
+    const int row = blockIdx.y * rq + threadIdx.x % rq, sub = threadIdx.x / rq;
     uint32_t n = 0;
     if (row < R)
         for (int p = sub; p < spp; p += nsub) n += cnt_part[((int64_t)slab * spp + p) * rp + row];
     red[threadIdx.x] = n;
     __syncthreads();
     if (sub == 0 && row < R) {
-        for (int s2 = 1; s2 < nsub; ++s2) n += red[s2 * rq + row];
-        n_below[row_out(slab, row, w, B, Hq, Hkv, G)] = (int32_t)n;
+        for (int s2 = 1; s2 < nsub; ++s2) n += red[s2 * rq + threadIdx.x % rq];
+        n_below[m.out(slab, row)] = (int32_t)n;
     }
 }
 
@@ -687,8 +722,8 @@ hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, h
     a.n_range = a.N;
     a.n_seg = a.S * plan.spp1;
     hipLaunchKernelGGL(f1, dim3((unsigned)(a.n_seg < plan.n_wg ? a.n_seg : plan.n_wg)), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.part, plan.spp1, plan.rp, a.R,
-                       a.w, a.B, a.Hq, a.Hkv, a.G, a.lse2, lse_out);
+    hipLaunchKernelGGL(stream_merge_kernel, merge_grid(a), dim3(256), 0, st, a.part, plan.spp1, plan.rp,
+                       row_map(a), a.lse2, lse_out);
     return launch_stream_pass2(plan, a, st);
 }
 
@@ -704,11 +739,11 @@ hipError_t launch_stream_stats(const StreamPlan& plan, StreamArgs a, float* lse_
     a.n_seg = a.S * plan.spp1;
     const unsigned grid = (unsigned)(a.n_seg < plan.n_wg ? a.n_seg : plan.n_wg);
     hipLaunchKernelGGL(f1, dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(stream_merge_st_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.part4, plan.spp1, plan.rp,
-                       a.R, a.w, a.B, a.Hq, a.Hkv, a.G, a.c, a.lse2, lse_out, entropy, sum_p2);
+    hipLaunchKernelGGL(stream_merge_st_kernel, merge_grid(a), dim3(256), 0, st, a.part4, plan.spp1, plan.rp,
+                       row_map(a), a.c, a.lse2, lse_out, entropy, sum_p2);
     hipLaunchKernelGGL(f2, dim3(grid), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(stream_count_kernel, dim3((unsigned)a.S), dim3(256), 0, st, a.cnt_part, plan.spp1, plan.rp,
-                       a.R, a.w, a.B, a.Hq, a.Hkv, a.G, n_below);
+    hipLaunchKernelGGL(stream_count_kernel, merge_grid(a), dim3(256), 0, st, a.cnt_part, plan.spp1, plan.rp,
+                       row_map(a), n_below);
     return hipGetLastError();
 }
 
