@@ -139,42 +139,53 @@ __global__ void csm_flag_kernel(CsmGeom g, const int32_t* chosen, uint8_t* flags
     }
 }
 
-// offsets[S][n_chunks]: survivors of the slab's earlier chunks (one
-// work-group per slab; a chunk of length len loses its chosen A tokens).
+// offsets[S][n_chunks]: survivors of the slab's earlier chunks. One
+// work-group per slab walks its chunks 256 at a time: a thread per chunk
+// counts the chunk's survivors (its length less its chosen A tokens, flag
+// bytes read four at a time where the chunks' flag runs are 4-byte aligned)
+// and a block scan turns the counts into offsets.
 __global__ void __launch_bounds__(256) csm_offsets_kernel(CsmGeom g, const uint8_t* flags, int32_t* offsets) {
-    __shared__ int32_t part[256];
+    __shared__ int32_t wsum[4];
     const int slab = blockIdx.x;
-    const int per = (g.n_chunks + 255) / 256;
-    const int c0 = threadIdx.x * per;
-    const int c1 = min(c0 + per, g.n_chunks);
-    int32_t sum = 0;
-    for (int c = c0; c < c1; ++c) {
-        int64_t start;
-        int len;
-        chunk_range(g, c, start, len);
-        int removed = 0;
-        const uint8_t* f = flags + (int64_t)slab * g.n_a + (int64_t)c * (g.C >> 1);
-        for (int i = 0; i < (len + 1) >> 1; ++i) removed += f[i];
-        sum += len - removed;
-    }
-    part[threadIdx.x] = sum;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
-        const int32_t t = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = g.C >> 1;
+    const bool words = half % 4 == 0 && g.n_a % 4 == 0;
+    int32_t carry = 0;
+    for (int c0 = 0; c0 < g.n_chunks; c0 += 256) {
+        const int c = c0 + threadIdx.x;
+        int32_t surv = 0;
+        if (c < g.n_chunks) {
+            int64_t start;
+            int len;
+            chunk_range(g, c, start, len);
+            const int na = (len + 1) >> 1;
+            const uint8_t* f = flags + (int64_t)slab * g.n_a + (int64_t)c * half;
+            int removed = 0, i = 0;
+            if (words) {
+                const uint32_t* fw = reinterpret_cast<const uint32_t*>(f);
+                for (; i + 4 <= na; i += 4) removed += (int)((fw[i >> 2] * 0x01010101u) >> 24);  // bytes are 0 or 1
+            }
+            for (; i < na; ++i) removed += f[i];
+            surv = len - removed;
+        }
+        int32_t incl = surv;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) wsum[wave] = incl;
         __syncthreads();
-        part[threadIdx.x] += t;
-        __syncthreads();
-    }
-    int32_t run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0;
-    for (int c = c0; c < c1; ++c) {
-        offsets[(int64_t)slab * g.n_chunks + c] = run;
-        int64_t start;
-        int len;
-        chunk_range(g, c, start, len);
-        int removed = 0;
-        const uint8_t* f = flags + (int64_t)slab * g.n_a + (int64_t)c * (g.C >> 1);
-        for (int i = 0; i < (len + 1) >> 1; ++i) removed += f[i];
-        run += len - removed;
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const int32_t t = wsum[w2];
+            if (w2 < wave) before += t;
+            total += t;
+        }
+        if (c < g.n_chunks) offsets[(int64_t)slab * g.n_chunks + c] = carry + before + incl - surv;
+        carry += total;
+        __syncthreads();  // wsum is rewritten by the next tile
     }
 }
 
