@@ -32,10 +32,13 @@ namespace {
 
 constexpr int kDecWaves = 4;
 constexpr int kMaxG = 8;
-// rows per lane in a block: 4, or 2 for groups of more than 4 heads
-template <int G>
+// Rows per lane in a block, so that each wave keeps enough key and value
+// slices in flight: 4; 8 for head dim 128 with 3 or 4 heads per group (at two
+// waves per SIMD: 7-10% faster than 4 rows at three waves); 2 for groups of
+// more than 4 heads, whose per-head state fills the registers.
+template <int D, int G>
 constexpr int rows_per_lane() {
-    return G <= 4 ? 4 : 2;
+    return G <= 2 ? 4 : G <= 4 ? (D == 128 ? 8 : 4) : 2;
 }
 
 struct DecGeom {
@@ -116,7 +119,7 @@ __device__ __forceinline__ float elem(const Slice<EL>& s, int e) {
 // registers a wave); also the resident work-groups per CU the host plans for
 // (a work-group has one wave per SIMD).
 __host__ __device__ constexpr int dec_waves(int d, int G) {
-    return d == 128 ? (G <= 2 ? 4 : G <= 5 ? 3 : 2) : (G <= 4 ? 4 : 3);
+    return d == 128 ? (G <= 2 ? 4 : G <= 4 ? 2 : G <= 5 ? 3 : 2) : (G <= 4 ? 4 : 3);
 }
 
 template <int D, int G>
@@ -130,7 +133,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
                                                      const int32_t* __restrict__ degree, float* part_m,
                                                      float* part_l, float* part_acc) {
     constexpr int EL = D / 16;  // elements of a row per lane
-    constexpr int kT = rows_per_lane<G>();
+    constexpr int kT = rows_per_lane<D, G>();
     constexpr int kBlock = 4 * kT;  // rows per wave and block
     __shared__ float red_m[kDecWaves][G], red_l[kDecWaves][G];
     __shared__ float red_acc[kDecWaves][G][D];
