@@ -16,8 +16,11 @@
 //   hist(p)   per chunk: LDS histogram of digit p over keys matching the
 //             prefix chosen so far, added bin by bin (integer atomics, so the
 //             total is exact and order-independent) into hist[row][p][bins]
-//   select(p) per row: suffix-scan the bins, pick the digit holding the k-th
-//             key, update (prefix, remaining)
+//   select(p) suffix-scan the bins of pass p, pick the digit holding the
+//             k-th key, update (prefix, remaining): run by every work-group
+//             of the next kernel (hist(p+1), or count after the last pass) on
+//             the merged histogram, the row's first chunk also recording the
+//             result in state[row][p]
 //   count     per chunk: keys above T and equal to T
 //   write     per chunk: exclusive offsets from the earlier chunks' counts,
 //             then an in-order block scan that writes kept positions.
@@ -62,7 +65,7 @@ struct TopkGeom {
     int32_t chunks;     // chunks per row
     int64_t chunk_len;  // elements per chunk (the last one may be shorter)
     uint32_t* hist;     // [rows][kPasses][kBins], zeroed by the window kernel
-    uint32_t* state;    // [rows][2]: prefix, remaining
+    uint32_t* state;    // [rows][kPasses][2]: prefix, remaining after each pass
     uint32_t* counts;   // [rows][chunks][2]: keys above T, keys equal to T
 };
 
@@ -73,12 +76,73 @@ __device__ __forceinline__ void chunk_range(const TopkGeom& g, int chunk, int64_
     if (b > g.Np) b = g.Np;
 }
 
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// select(p) by the whole block: scan the merged histogram of pass p and choose
+// the digit that holds the k-th largest key among those still matching; every
+// thread gets the new (prefix, remaining). The row's first chunk records them
+// in state[row][p] for the kernels after the next one.
+__device__ void block_select(const TopkGeom& g, int64_t row, int pass, int chunk, uint32_t& prefix,
+                             uint32_t& remaining) {
+    constexpr int PER = kBins / kThreads;  // 8 consecutive digits per thread, highest first
+    __shared__ uint32_t wsum[kThreads / 64];
+    __shared__ uint32_t res[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t c[PER];
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int d = kBins - 1 - (tid * PER + k);
+        c[k] = g.hist[(row * kPasses + pass) * kBins + d];
+        tot += c[k];
+    }
+    const uint32_t incl = wave_inclusive_scan(tot, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t above = incl - tot;  // keys in digits above this thread's first digit
+    for (int w2 = 0; w2 < wave; ++w2) above += wsum[w2];
+    // exactly one digit holds the k-th key (remaining <= the keys still matching)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int d = kBins - 1 - (tid * PER + k);
+        if (above < remaining && above + c[k] >= remaining) {
+            res[0] = prefix | ((uint32_t)d << digit_shift(pass));
+            res[1] = remaining - above;
+        }
+        above += c[k];
+    }
+    __syncthreads();
+    prefix = res[0];
+    remaining = res[1];
+    if (chunk == 0 && tid == 0) {
+        g.state[(row * kPasses + pass) * 2] = prefix;
+        g.state[(row * kPasses + pass) * 2 + 1] = remaining;
+    }
+}
+
+// (prefix, remaining) after pass p - 1 = select(p - 1) on the state after
+// pass p - 2 (the initial one for pass 0: no prefix, kk to find).
+__device__ __forceinline__ void state_after(const TopkGeom& g, int64_t row, int p1, int chunk, uint32_t& prefix,
+                                            uint32_t& remaining) {
+    prefix = p1 == 0 ? 0u : g.state[(row * kPasses + p1 - 1) * 2];
+    remaining = p1 == 0 ? (uint32_t)g.kk : g.state[(row * kPasses + p1 - 1) * 2 + 1];
+    block_select(g, row, p1, chunk, prefix, remaining);
+}
+
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkGeom g, int pass) {
     __shared__ uint32_t h[kBins];
     const int chunk = blockIdx.x;
     const int64_t row = blockIdx.y;
     for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
-    const uint32_t prefix = pass == 0 ? 0u : g.state[row * 2];
+    uint32_t prefix = 0u, remaining = (uint32_t)g.kk;
+    if (pass > 0) state_after(g, row, pass - 1, chunk, prefix, remaining);
     const uint32_t pm = prefix_mask(pass);
     const int shift = digit_shift(pass);
     const uint32_t dm = digit_mask(pass);
@@ -105,54 +169,12 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(TopkGeom g, int pas
         if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    return v;
-}
-
-// One work-group per row: scan the merged histogram of pass p and choose
-// the digit that holds the k-th largest key among those still matching.
-__global__ __launch_bounds__(kThreads) void topk_select_kernel(TopkGeom g, int pass) {
-    constexpr int PER = kBins / kThreads;  // 8 consecutive digits per thread, highest first
-    __shared__ uint32_t wsum[kThreads / 64];
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t prefix = pass == 0 ? 0u : g.state[row * 2];
-    const uint32_t remaining = pass == 0 ? (uint32_t)g.kk : g.state[row * 2 + 1];
-    uint32_t c[PER];
-    uint32_t tot = 0u;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int d = kBins - 1 - (tid * PER + k);
-        c[k] = g.hist[(row * kPasses + pass) * kBins + d];
-        tot += c[k];
-    }
-    const uint32_t incl = wave_inclusive_scan(tot, lane);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t above = incl - tot;  // keys in digits above this thread's first digit
-    for (int w2 = 0; w2 < wave; ++w2) above += wsum[w2];
-    __syncthreads();  // every thread has read the state before it changes
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int d = kBins - 1 - (tid * PER + k);
-        if (above < remaining && above + c[k] >= remaining) {
-            g.state[row * 2] = prefix | ((uint32_t)d << digit_shift(pass));
-            g.state[row * 2 + 1] = remaining - above;
-        }
-        above += c[k];
-    }
-}
-
 __global__ __launch_bounds__(kThreads) void topk_count_kernel(TopkGeom g) {
     __shared__ uint32_t red[2][kThreads / 64];
     const int chunk = blockIdx.x;
     const int64_t row = blockIdx.y;
-    const uint32_t T = g.state[row * 2];
+    uint32_t T, take_eq;
+    state_after(g, row, kPasses - 1, chunk, T, take_eq);
     int64_t b, e;
     chunk_range(g, chunk, b, e);
     const uint32_t* x = g.x + row * g.Np;
@@ -205,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkGeom g) {
     const int chunk = blockIdx.x;
     const int64_t row = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t T = g.state[row * 2];
-    const uint32_t take_eq = g.state[row * 2 + 1];
+    const uint32_t T = g.state[(row * kPasses + kPasses - 1) * 2];
+    const uint32_t take_eq = g.state[(row * kPasses + kPasses - 1) * 2 + 1];
     int32_t* out = g.idx + row * (int64_t)g.budget;
     {
         // counts of the chunks before this one, summed by the whole block
@@ -323,7 +345,8 @@ size_t topk_workspace_bytes(int32_t rows, int64_t Np) {
     int32_t chunks;
     int64_t chunk_len;
     plan_chunks(rows, Np > 0 ? Np : 1, chunks, chunk_len);
-    return align256((size_t)rows * kPasses * kBins * sizeof(uint32_t)) + align256((size_t)rows * 2 * sizeof(uint32_t)) +
+    return align256((size_t)rows * kPasses * kBins * sizeof(uint32_t)) +
+           align256((size_t)rows * kPasses * 2 * sizeof(uint32_t)) +
            align256((size_t)rows * chunks * 2 * sizeof(uint32_t));
 }
 
@@ -345,7 +368,7 @@ hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t bud
         g.hist = reinterpret_cast<uint32_t*>(p);
         p += align256((size_t)rows * kPasses * kBins * sizeof(uint32_t));
         g.state = reinterpret_cast<uint32_t*>(p);
-        p += align256((size_t)rows * 2 * sizeof(uint32_t));
+        p += align256((size_t)rows * kPasses * 2 * sizeof(uint32_t));
         g.counts = reinterpret_cast<uint32_t*>(p);
     }
     int64_t work = (int64_t)rows * window;
@@ -357,10 +380,8 @@ hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t bud
                        g.hist);
     if (g.kk > 0) {
         const dim3 grid((unsigned)g.chunks, (unsigned)rows);
-        for (int pass = 0; pass < kPasses; ++pass) {
+        for (int pass = 0; pass < kPasses; ++pass)
             hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, st, g, pass);
-            hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, g, pass);
-        }
         hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, st, g);
         hipLaunchKernelGGL(topk_write_kernel, grid, dim3(kThreads), 0, st, g);
     }
