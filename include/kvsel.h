@@ -100,7 +100,7 @@ size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc);
  * workspace  device, >= kvsel_score_workspace_bytes(desc) bytes, 256-byte
  *         aligned; its content is scratch between calls.
  * Paths: bf16 with head_dim 64/128 and w <= 256 streams K in two passes
- * (when G*w > 256 the group's query heads are streamed in row groups of at
+ * (when G*w > 256 the group's query heads are streamed in head groups of at
  * most 256 rows, each reading the keys); other shapes take a general
  * two-pass path. The environment variable
  * KVSEL_SCORE_PATH=resident (register-resident, single K read) or =general

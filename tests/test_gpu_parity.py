@@ -35,7 +35,7 @@ RAGGED = [
     ("bf16", 1, 1, 4, 1, 128, 3001, 5, 7, 300),     # ragged last chunk, G=4, w=5 -> 20 rows
     ("bf16", 2, 2, 6, 2, 64, 2500, 7, 3, 999),      # G=3, 21 rows, 2 layers
     ("bf16", 1, 1, 28, 4, 128, 4100, 16, 7, 512),   # G=7 -> 112 rows (7 row blocks)
-    ("bf16", 1, 1, 14, 1, 128, 1500, 20, 7, 100),   # 280 rows: streamed as 2 row groups of 7 heads
+    ("bf16", 1, 1, 14, 1, 128, 1500, 20, 7, 100),   # 280 rows: streamed as 2 head groups of 7 heads
     ("bf16", 1, 1, 8, 8, 128, 1111, 1, 1, 1),       # w=1, budget=w, G=1
     ("bf16", 1, 1, 8, 2, 128, 777, 64, 5, 777),     # budget = N
     ("bf16", 1, 2, 4, 2, 128, 40, 40, 7, 40),       # w = N: empty prefix
@@ -43,7 +43,7 @@ RAGGED = [
     ("f32", 1, 1, 8, 2, 64, 2049, 32, 7, 256),      # fp32, ragged
     ("f32", 3, 1, 4, 2, 128, 1300, 9, 3, 60),       # fp32 d=128, 3 layers
     ("f32", 1, 1, 12, 4, 64, 5000, 33, 1, 4000),    # fp32, pool 1, large budget
-    ("bf16", 1, 1, 64, 8, 128, 2048, 128, 7, 1024), # 1024 rows: 4 row groups of 2 heads
+    ("bf16", 1, 1, 64, 8, 128, 2048, 128, 7, 1024), # 1024 rows: 4 head groups of 2 heads
     ("bf16", 2, 1, 28, 4, 64, 3333, 64, 7, 400),    # G=7, w=64 (448 rows): groups of 4 and 3 heads, 2 layers
 ]
 

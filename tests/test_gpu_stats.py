@@ -89,7 +89,7 @@ SHAPES = [
     (1, 1, 8, 2, 128, 777, 64, 5),      # 256 rows
     (1, 2, 4, 2, 128, 40, 40, 7),       # w = N: no prefix, only window keys
     (1, 1, 4, 2, 128, 41, 40, 7),       # one prefix key
-    (2, 1, 28, 4, 64, 2100, 64, 7),     # 448 rows: row groups of 4 and 3 heads, 2 layers
+    (2, 1, 28, 4, 64, 2100, 64, 7),     # 448 rows: head groups of 4 and 3 heads, 2 layers
 ]
 
 

@@ -95,7 +95,7 @@ struct Plan {
     int RB;
     ScoreWs gen;               // general two-pass layout (any dtype)
     kvsel::StreamPlan stream;  // streaming bf16 layout (stream.ok when eligible)
-    int T, Gs;                 // streaming row groups: T groups of at most Gs query heads per KV head
+    int T, Gs;                 // streaming head groups: T groups of at most Gs query heads per KV head
     kvsel::KresPlan kres;      // register-resident bf16 layout (kres.ok when eligible)
     size_t stream_total, kres_total, total;
 };
@@ -104,10 +104,10 @@ size_t raw_bytes(int64_t S, int64_t Np) { return ((size_t)S * Np * sizeof(float)
 size_t raw_bytes(const ScoreGeom& g) { return raw_bytes(g.S, g.Np); }
 
 // The streaming kernels hold at most 256 window rows per slab. Past that, a
-// KV head's query heads split into T row groups of at most Gs heads each
+// KV head's query heads split into T head groups of at most Gs heads each
 // (Gs*w <= 256, sizes balanced), each streamed as a slab of its own over the
 // same keys; their raw scores add up like extra layers.
-void row_groups(const ScoreGeom& g, int& T, int& Gs) {
+void head_groups(const ScoreGeom& g, int& T, int& Gs) {
     T = 1;
     Gs = g.G;
     if (g.R <= 256 || g.w > 256) return;
@@ -122,7 +122,7 @@ void make_plan(const kvsel_score_desc_t* d, Plan& p) {
     p.total = p.gen.total;
     const int n_cu = device_cu_count();
     p.stream_total = p.kres_total = 0;
-    row_groups(p.g, p.T, p.Gs);
+    head_groups(p.g, p.T, p.Gs);
     const int64_t S_groups = (int64_t)p.g.S * p.T;
     p.stream.ok = false;
     if (S_groups <= 65535 &&
@@ -178,7 +178,7 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
     g.lse_out = lse_out;
     g.lse_in = lse_in;
     float* raw = nullptr;
-    int raw_layers = g.L;  // slices of raw that the pool sums (layers, times row groups)
+    int raw_layers = g.L;  // slices of raw that the pool sums (layers, times head groups)
     bool done = false;
     if (stats && !p.stream.ok) return KVSEL_ERR_UNSUPPORTED;  // the statistics ride on the streaming passes
     Path path = stats ? Path::Stream : choose_path(p);
@@ -226,7 +226,7 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         raw = a.raw;
         raw_layers = g.L * p.T;
         if (p.T > 1 && desc->pool_type == KVSEL_POOL_MAX && g.Np > 0) {
-            // the max pool is not linear: add the row groups into the first
+            // the max pool is not linear: add the head groups into the first
             // group's slices first, then pool layer by layer
             for (int t = 1; t < p.T; ++t)
                 if (kvsel::launch_accumulate(1, g.S, g.Np, raw + (int64_t)t * g.S * g.Np, raw, KVSEL_ACC_ADD, hs) !=

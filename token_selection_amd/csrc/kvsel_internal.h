@@ -45,7 +45,7 @@ hipError_t launch_score_passes(const ScoreGeom& g, int dtype, int head_dim, int 
 
 // Row LSE2 [S][stride] (log2 domain, +inf past R) from a handed-in natural-log
 // LSE [L][B][Hq][w].
-// Slabs are [T][S0] row groups of Gs heads each (T = 1, Gs = G without
+// Slabs are [T][S0] head groups of Gs heads each (T = 1, Gs = G without
 // groups); R is the row count of a full group.
 hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int stride, int R, int w, int B, int Hq,
                                  int Hkv, int G, int S0, int Gs, hipStream_t stream);
@@ -98,7 +98,7 @@ struct StreamArgs {
     int64_t ks[4];
     int32_t B, Hq, Hkv, G, w, R;
     int32_t N, Np, S;
-    // Row groups: when the G*w rows of a KV head exceed the kernels' 256,
+    // Head groups: when the G*w rows of a KV head exceed the kernels' 256,
     // its query heads split into T groups of Gs heads (the last may hold
     // fewer), each a slab of its own. Slabs are [T][S0] with S0 = L*B*Hkv;
     // R = Gs*w is the row count of a full group.

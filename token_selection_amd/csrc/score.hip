@@ -401,7 +401,7 @@ __global__ void lse_from_input_kernel(const float* lse_in, float* lse2, int S, i
     const int s = blockIdx.y;
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= S || r >= stride) return;
-    const int t = s / S0, s0 = s - t * S0;  // row group, (layer, b, kv head) slab
+    const int t = s / S0, s0 = s - t * S0;  // head group, (layer, b, kv head) slab
     const int rows = min(Gs, G - t * Gs) * w;
     float v = INFINITY;
     if (r < rows && r < R) {

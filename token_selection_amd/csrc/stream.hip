@@ -19,7 +19,7 @@
 // that are summed over the lanes once per segment.
 //
 // A slab holds at most 256 window rows: when a KV head's G*w rows exceed
-// that, its query heads split into row groups, each a slab of its own over
+// that, its query heads split into head groups, each a slab of its own over
 // the same keys (StreamArgs::T, Gs, S0).
 //
 // No work-group waits for another: every slab is cut into segments of whole
@@ -133,7 +133,7 @@ __device__ __forceinline__ Cursor advance(const StreamArgs& a, Cursor c) {
     return Cursor{-1, 0, 0};
 }
 
-// Slabs are [T][S0]: row group t = slab / S0 of the (layer, b, KV head)
+// Slabs are [T][S0]: head group t = slab / S0 of the (layer, b, KV head)
 // slab s0 = slab % S0 (s0 = (l*B + b)*Hkv + g) holds query heads
 // g*G + t*Gs + (0 .. slab_rows/w - 1).
 __device__ __forceinline__ const uint16_t* slab_keys(const StreamArgs& a, int slab) {
@@ -190,7 +190,7 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
     const int g = s0 % a.Hkv;
     const int b = (s0 / a.Hkv) % a.B;
     const int l = s0 / (a.Hkv * a.B);
-    const int h0 = g * a.G + slab / a.S0 * a.Gs;  // the row group's first query head
+    const int h0 = g * a.G + slab / a.S0 * a.Gs;  // the head group's first query head
     const int rows = slab_rows(a, slab);
     const uint16_t* qbase = a.q + l * a.qs[0] + b * a.qs[1];
     __syncthreads();  // every wave is done with the previous segment's rows
