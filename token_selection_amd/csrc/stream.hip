@@ -677,14 +677,21 @@ int pow2_at_least(int x) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Segments per slab for `keys` keys: about two per work-group slot of the
-// grid in total, each a whole number of chunks.
+// Segments per slab for `keys` keys, each a whole number of chunks: as few
+// as keep every segment within kMaxSegChunks, at most m per work-group slot
+// of the grid in total for the smallest such m (m = 1 unless the slabs are
+// long), so that no work-group stages a slab's rows more often than it must
+// and none takes an extra full segment.
 void segments(int64_t keys, int64_t S, int n_wg, int& spp, int& seg_len) {
-    int64_t want = (2 * (int64_t)n_wg + S - 1) / S;
     const int64_t chunks = (keys + kChunk - 1) / kChunk;
-    if (want > chunks) want = chunks;
-    if (want < 1) want = 1;
-    int64_t per = (chunks + want - 1) / want;  // chunks per segment
+    int64_t per = chunks;  // chunks per segment
+    for (int64_t m = 1;; ++m) {
+        int64_t want = m * n_wg / S;
+        if (want > chunks) want = chunks;
+        if (want < 1) want = 1;
+        per = (chunks + want - 1) / want;
+        if (per <= kMaxSegChunks || want == chunks) break;
+    }
     if (per > kMaxSegChunks) per = kMaxSegChunks;
     seg_len = (int)(per * kChunk);
     spp = (int)((keys + seg_len - 1) / seg_len);
