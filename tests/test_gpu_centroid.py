@@ -189,6 +189,11 @@ DEC_CASES = [
     (1, 32, 8, 5000, 128, True),
     (2, 2, 2, 1, 128, False),      # a single key
     (1, 8, 1, 70000, 64, True),    # many splits, G = 8
+    (2, 6, 2, 3001, 128, True),    # G = 3 (8 rows per lane), ragged
+    (1, 16, 4, 33, 128, True),     # G = 4, fewer keys than one 8-row block per wave
+    (1, 4, 2, 4100, 128, False),   # G = 2
+    (1, 10, 2, 777, 128, False),   # G = 5
+    (2, 12, 2, 2049, 128, True),   # G = 6
 ]
 
 
