@@ -194,6 +194,7 @@ DEC_CASES = [
     (1, 4, 2, 4100, 128, False),   # G = 2
     (1, 10, 2, 777, 128, False),   # G = 5
     (2, 12, 2, 2049, 128, True),   # G = 6
+    (1, 16, 2, 1500, 128, True),   # G = 8
 ]
 
 
