@@ -16,7 +16,8 @@
 //                      the chunk as one 32x32 tile of 32x32x16 MFMAs (A keys
 //                      as the B operand, so a lane is an A token and its
 //                      registers are B tokens), the best B of each A (ties to
-//                      the lower position) -> score, match.
+//                      the lower position) -> score, match, and the A token's
+//                      flag cleared.
 //   (kvsel top-k)      the n_merge best scores of each slab, ties to the lower
 //                      A index (the selection kernels with no window).
 //   csm_flag_kernel    marks the chosen A tokens.
@@ -61,7 +62,7 @@ __device__ __forceinline__ void chunk_range(const CsmGeom& g, int c, int64_t& st
 
 template <int D>
 __global__ void __launch_bounds__(256) csm_match_kernel(CsmGeom g, const uint16_t* __restrict__ k, float* score,
-                                                        int32_t* match) {
+                                                        int32_t* match, uint8_t* flags) {
     constexpr int KS = D / 16;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -122,15 +123,11 @@ __global__ void __launch_bounds__(256) csm_match_kernel(CsmGeom g, const uint16_
         const int64_t ai = (int64_t)slab * g.n_a + (int64_t)c * (g.C >> 1) + col;
         score[ai] = best;
         match[ai] = best_j >= 0 ? (int32_t)(start + 2 * best_j + 1) : -1;
+        flags[ai] = 0;  // every A slot is written here: the chosen ones are flagged after the ranking
     }
 }
 
-// flags[S][n_a] = 1 for the chosen A tokens (the flags were zeroed first).
-__global__ void csm_clear_kernel(uint8_t* flags, int64_t total) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x)
-        flags[i] = 0;
-}
-
+// flags[S][n_a] = 1 for the chosen A tokens (the match kernel zeroed them all).
 __global__ void csm_flag_kernel(CsmGeom g, const int32_t* chosen, uint8_t* flags) {
     const int64_t total = (int64_t)g.S * g.n_merge;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -414,12 +411,9 @@ hipError_t launch_csm(int32_t S, int64_t n, int32_t d, int32_t C, int32_t n_sink
     const dim3 cgrid((unsigned)((g.n_chunks + kCsmWaves - 1) / kCsmWaves), (unsigned)S);
     if (g.n_chunks > 0) {
         if (d == 128)
-            hipLaunchKernelGGL(csm_match_kernel<128>, cgrid, dim3(256), 0, st, g, k, score, match);
+            hipLaunchKernelGGL(csm_match_kernel<128>, cgrid, dim3(256), 0, st, g, k, score, match, flags);
         else
-            hipLaunchKernelGGL(csm_match_kernel<64>, cgrid, dim3(256), 0, st, g, k, score, match);
-        const int64_t nf = (int64_t)S * g.n_a;
-        hipLaunchKernelGGL(csm_clear_kernel, dim3(blocks_for(nf)), dim3(256), 0,
-                           st, flags, nf);
+            hipLaunchKernelGGL(csm_match_kernel<64>, cgrid, dim3(256), 0, st, g, k, score, match, flags);
         if (n_merge > 0) {
             const hipError_t e =
                 launch_topk(S, g.n_a, 0, n_merge, 0, score, chosen, ws + w.topk_off, st);
