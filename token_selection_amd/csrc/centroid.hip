@@ -42,6 +42,8 @@ namespace {
 
 using namespace tile;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kCsmWaves = 4;  // chunks per work-group
 
 struct CsmGeom {
@@ -81,23 +83,32 @@ __global__ void __launch_bounds__(256) csm_match_kernel(CsmGeom g, const uint16_
     const int64_t pa = start + 2 * min(col, na - 1);
     const int64_t pb = start + 2 * min(col, max(nb, 1) - 1) + (nb > 0 ? 1 : 0);
     bf16x8 fa[KS], fb[KS];
-    float sa = 0.f, sb = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         fa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks + pa * D + s * 16 + hf * 8));
         fb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks + pb * D + s * 16 + hf * 8));
+    }
+    // |k|^2 of A token col and of B token col: bf16 pairs squared and summed in fp32 (v_dot2)
+    float sa = 0.f, sb = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xa = (float)fa[s][e];
-            const float xb = (float)fb[s][e];
-            sa += xa * xa;
-            sb += xb * xb;
+    for (int s = 0; s < KS; ++s) {
+        const uint4 ua = __builtin_bit_cast(uint4, fa[s]);
+        const uint4 ub = __builtin_bit_cast(uint4, fb[s]);
+        const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w};
+        const uint32_t wb[4] = {ub.x, ub.y, ub.z, ub.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const bf16x2 xa = __builtin_bit_cast(bf16x2, wa[h]);
+            const bf16x2 xb = __builtin_bit_cast(bf16x2, wb[h]);
+            sa = __builtin_amdgcn_fdot2_f32_bf16(xa, xa, sa, false);
+            sb = __builtin_amdgcn_fdot2_f32_bf16(xb, xb, sb, false);
         }
     }
-    sa += __shfl_xor(sa, 32);  // |k|^2 of A token col and of B token col
+    sa += __shfl_xor(sa, 32);
     sb += __shfl_xor(sb, 32);
-    const float norm_a = sqrtf(sa);
-    const float norm_b = sqrtf(sb);
+    // 1/|k| (0 for a zero key, whose cosine with anything is taken as 0)
+    const float inv_a = sa > 0.f ? __builtin_amdgcn_rsqf(sa) : 0.f;
+    const float inv_b = sb > 0.f ? __builtin_amdgcn_rsqf(sb) : 0.f;
     // dot[A col][B tile_row(v, hf)]: B keys as the A operand (rows), A keys as the B operand (lanes)
     const f32x16 dot = logits<KS>(fb, fa);
     float best = -INFINITY;
@@ -105,9 +116,7 @@ __global__ void __launch_bounds__(256) csm_match_kernel(CsmGeom g, const uint16_
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int j = tile_row(v, hf);  // ascending in v for a fixed half
-        const float nbj = __shfl(norm_b, j);
-        const float den = norm_a * nbj;
-        const float sim = den > 0.f ? dot[v] / den : 0.f;
+        const float sim = dot[v] * (inv_a * __shfl(inv_b, j));
         if (j < nb && sim > best) {
             best = sim;
             best_j = j;
