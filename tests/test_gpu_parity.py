@@ -170,6 +170,26 @@ def test_accumulate_flag_adds_layers():
     assert_scores_close(acc.cpu().numpy(), ref["scores"])
 
 
+@pytest.mark.parametrize("pool_type", [K.KVSEL_POOL_AVG, K.KVSEL_POOL_MAX])
+def test_accumulate_with_head_groups(pool_type):
+    """Accumulation across calls with 448 window rows per KV head (G = 7,
+    w = 64: two head groups): two calls of 2 layers equal one call of 4 layers
+    and the oracle's layer sum, with either pool."""
+    wl = TINY.with_(name="acc_hg", wid=145, dtype="bf16", head_dim=128, n_layers=4, n_q_heads=28, n_kv_heads=4,
+                    n_keys=1500, window=64, kv_budget=300, n_hubs=20)
+    say("case accumulate head groups", pool_type)
+    inp = make_inputs(wl)
+    ref = oracle_for(wl, inp, pool_type=pool_type)
+    q = to_dev(inp["q"], "bf16")
+    k = to_dev(inp["k"], "bf16")
+    s1 = K.kvsel_score(q[:2], k[:2], window=wl.window, pool_kernel=7, pool_type=pool_type)
+    K.kvsel_score(q[2:], k[2:], s1, window=wl.window, pool_kernel=7, pool_type=pool_type, accumulate=True)
+    s4 = K.kvsel_score(q, k, window=wl.window, pool_kernel=7, pool_type=pool_type)
+    torch.cuda.synchronize()
+    assert_scores_close(s1.cpu().numpy(), ref["scores"])
+    assert_scores_close(s4.cpu().numpy(), ref["scores"])
+
+
 def test_exact_ties_follow_tie_break():
     """q = 0 makes every prefix score bit-identical on the GPU too; the
     tie-break alone decides: pool 1 keeps [0, kk), pool 7 keeps [3, kk + 3)."""
