@@ -79,14 +79,33 @@ __global__ void __launch_bounds__(256) csm_match_kernel(CsmGeom g, const uint16_
     const int na = (len + 1) >> 1;
     const int nb = len >> 1;
     const uint16_t* ks = k + (int64_t)slab * g.n * D;
-    // lane (col, hf): A token col and B token col (clamped into the chunk)
-    const int64_t pa = start + 2 * min(col, na - 1);
-    const int64_t pb = start + 2 * min(col, max(nb, 1) - 1) + (nb > 0 ? 1 : 0);
+    // Each load instruction reads 32 consecutive rows of the chunk, 32 bytes
+    // of each (a faster pattern than every other row): lane col < 16 takes
+    // row 2*col (A token col), lane col >= 16 row 2*(col-16) + 1 (B token
+    // col-16), in the first 32 rows (x) and the next 32 (y); rows past the
+    // chunk read its last row (those tokens are masked). Swapping x's lanes
+    // 16-31 with y's lanes 0-15 (and 48-63 with 32-47) leaves A tokens 0-31
+    // in x and B tokens 0-31 in y: lane (col, hf) holds A token col and B
+    // token col, head-dim elements s*16 + hf*8 .. +7.
+    const int r0 = col < 16 ? 2 * col : 2 * (col - 16) + 1;
+    const int64_t px = start + min(r0, len - 1);
+    const int64_t py = start + min(32 + r0, len - 1);
     bf16x8 fa[KS], fb[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        fa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks + pa * D + s * 16 + hf * 8));
-        fb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks + pb * D + s * 16 + hf * 8));
+        const uint4 x = *reinterpret_cast<const uint4*>(ks + px * D + s * 16 + hf * 8);
+        const uint4 y = *reinterpret_cast<const uint4*>(ks + py * D + s * 16 + hf * 8);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+        const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
+        uint32_t as[4], bs[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const auto r = __builtin_amdgcn_permlane16_swap(xs[h], ys[h], false, false);
+            as[h] = r[0];
+            bs[h] = r[1];
+        }
+        fa[s] = __builtin_bit_cast(bf16x8, make_uint4(as[0], as[1], as[2], as[3]));
+        fb[s] = __builtin_bit_cast(bf16x8, make_uint4(bs[0], bs[1], bs[2], bs[3]));
     }
     // |k|^2 of A token col and of B token col: bf16 pairs squared and summed in fp32 (v_dot2)
     float sa = 0.f, sb = 0.f;
