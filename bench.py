@@ -29,6 +29,9 @@ SCORE_SOURCES = ("token_selection_amd/csrc/stream.hip+token_selection_amd/csrc/s
                  "+token_selection_amd/csrc/tile32.h")
 # ... and with the pivot statistics, also the per-layer summary kernel
 STATS_SOURCES = SCORE_SOURCES + "+token_selection_amd/csrc/pivot.hip"
+# decode attention; one CentroidKV round (its ranking runs the top-k kernels)
+DECODE_SOURCES = "token_selection_amd/csrc/decode.hip"
+CSM_SOURCES = "token_selection_amd/csrc/centroid.hip+token_selection_amd/csrc/topk.hip"
 
 
 def recorded_traffic(kernel: str, sources: str):
@@ -356,7 +359,8 @@ def bench_extra(args, K, get_workload, make_inputs) -> int:
                            "decode_batch": L * B, "q_heads": Hq, "kv_heads": Hkv, "keys": bud, "head_dim": d},
                 "roofline": {"bound": "hbm", "kernel": "kvsel_decode_attention (decode_kernel + combine)",
                              "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                             "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                             "traffic": recorded_traffic("kvsel_decode_attention", DECODE_SOURCES),
                              "algorithmic_bytes": alg},
                 "cpu_baseline": cpu}
         print(json.dumps(line))
@@ -391,7 +395,8 @@ def bench_extra(args, K, get_workload, make_inputs) -> int:
                        "chunk": chunk, "n_sink": ns, "n_recent": nr, "rate": rate, "n_merge": nm},
             "roofline": {"bound": "hbm", "kernel": "kvsel_csm (match + select + merge)",
                          "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg},
+                         "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("kvsel_csm", CSM_SOURCES), "algorithmic_bytes": alg},
             "cpu_baseline": cpu}
     print(json.dumps(line))
     return 0
