@@ -313,6 +313,51 @@ def check_given_lse_mass_and_shift(orc):
                                    rtol=1e-12, atol=1e-300)
 
 
+def _bf16_bits(x):
+    """Round float64 values to bf16 (nearest-even) and return the bit patterns."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def _bits_to_f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_all_drivers_per_slice(orc):
+    """The per-(layer, sequence) drivers saliency_all_given_lse and
+    row_stats_all against the brute force of each slice: L = 2, B = 2 with
+    inputs that differ in every (l, b) (and LSE offsets that differ per row),
+    bf16 and fp32 storage, one worker thread and two. A swapped l/b index or
+    a wrong slice puts another slice's numbers in place and fails here."""
+    rng = np.random.default_rng(4321)
+    L, B, Hq, Hkv, w, d, N, tau = 2, 2, 4, 2, 3, 4, 11, 0.08
+    scale = 1.0 / math.sqrt(d)
+    for dtype in ("bf16", "f32"):
+        qf = rng.standard_normal((L, B, Hq, w, d)) * (1.0 + np.arange(L * B).reshape(L, B, 1, 1, 1))
+        kf = rng.standard_normal((L, B, Hkv, N, d)) + 0.3 * np.arange(L * B).reshape(L, B, 1, 1, 1)
+        if dtype == "bf16":
+            q, k = _bf16_bits(qf), _bf16_bits(kf)
+            qv, kv = _bits_to_f64(q), _bits_to_f64(k)
+        else:
+            q, k = qf.astype(np.float32), kf.astype(np.float32)
+            qv, kv = q.astype(np.float64), k.astype(np.float64)
+        lse = rng.normal(1.5, 1.0, size=(L, B, Hq, w)) + np.arange(L * B).reshape(L, B, 1, 1)
+        for threads in (1, 2):
+            raw = orc.saliency_all_given_lse(q, k, lse, dtype, threads=threads)
+            ent, sp2, nb = orc.row_stats_all(q, k, dtype, tau, threads=threads)
+            assert raw.shape == (L, B, Hkv, N) and ent.shape == sp2.shape == nb.shape == (L, B, Hq, w)
+            for l in range(L):
+                for b in range(B):
+                    braw = brute_saliency_given_lse(qv[l, b].tolist(), kv[l, b].tolist(), lse[l, b].tolist(),
+                                                    scale)
+                    np.testing.assert_allclose(raw[l, b], np.array(braw), rtol=1e-11, atol=1e-15)
+                    bent, bsp2, bnb = brute_row_stats(qv[l, b].tolist(), kv[l, b].tolist(), scale, tau)
+                    np.testing.assert_allclose(ent[l, b], np.array(bent), rtol=1e-12, atol=1e-14)
+                    np.testing.assert_allclose(sp2[l, b], np.array(bsp2), rtol=1e-12, atol=1e-14)
+                    assert nb[l, b].tolist() == bnb
+
+
 def check_max_pool(orc):
     """Max-pool variant: == the brute force on random rows; a lone spike of
     height h in a zero row becomes h on the 2r+1 positions around it (clipped
@@ -422,6 +467,7 @@ def check_layer_summary_and_pivot(orc):
 
 
 ALL_CHECKS = [
+    check_all_drivers_per_slice,
     check_row_stats_brute,
     check_row_stats_closed_forms,
     check_layer_summary_and_pivot,

@@ -60,6 +60,17 @@ MUTATIONS = {
                        "raw[h // G] += np.exp(logits + lse[h][:, None]).sum(axis=0)"),
     "given_lse_no_mean": ("    return raw / G\n\n\ndef saliency_all_given_lse", "    return raw\n\n\ndef saliency_all_given_lse"),
     "given_lse_wrong_group": ("logits = window_logits(q[h], k[h // G], scale)", "logits = window_logits(q[h], k[h % Hkv], scale)"),
+    "given_lse_all_lse_swapped": ("np.asarray(lse[l, b], dtype=np.float64), scale)",
+                                  "np.asarray(lse[b, l], dtype=np.float64), scale)"),
+    "given_lse_all_wrong_slice": ("raw[l, b] = saliency_given_lse(to_f64(q[l, b], dtype), to_f64(k[l, b], dtype),",
+                                  "raw[l, b] = saliency_given_lse(to_f64(q[l, b], dtype), to_f64(k[l, 0], dtype),"),
+    "given_lse_all_out_swapped": ("        raw[l, b] = saliency_given_lse(", "        raw[b, l] = saliency_given_lse("),
+    "stats_all_wrong_slice": ("row_stats(to_f64(q[l, b], dtype), to_f64(k[l, b], dtype), small_p, scale)",
+                              "row_stats(to_f64(q[l, b], dtype), to_f64(k[b, l], dtype), small_p, scale)"),
+    "stats_all_out_swapped": ("        ent[l, b], sp2[l, b], nb[l, b] = row_stats(",
+                              "        ent[b, l], sp2[b, l], nb[b, l] = row_stats("),
+    "stats_all_first_seq_only": ("    jobs = [(l, b) for l in range(L) for b in range(B)]\n    if threads <= 1:\n        for j in jobs:\n            unit(j)\n    else:\n        ctx = threadpool_limits(1) if threadpool_limits is not None else _null()\n        with ctx, cf.ThreadPoolExecutor(threads) as ex:\n            list(ex.map(unit, jobs))\n    return ent, sp2, nb",
+                                 "    jobs = [(l, b) for l in range(L) for b in range(1)]\n    if threads <= 1:\n        for j in jobs:\n            unit(j)\n    else:\n        ctx = threadpool_limits(1) if threadpool_limits is not None else _null()\n        with ctx, cf.ThreadPoolExecutor(threads) as ex:\n            list(ex.map(unit, jobs))\n    return ent, sp2, nb"),
 }
 
 
