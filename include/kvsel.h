@@ -55,6 +55,10 @@ typedef int32_t kvsel_status_t;
 #define KVSEL_POOL_AVG 0 /* stride-1 average pool, zero padded, divisor = kernel */
 #define KVSEL_POOL_MAX 1 /* stride-1 max pool over the positions inside [0, N-w), per layer */
 
+#define KVSEL_PATH_AUTO 0    /* streaming kernels where they apply, else the general ones */
+#define KVSEL_PATH_STREAM 1  /* streaming two-pass kernels: bf16, head_dim 64/128, w <= 256 */
+#define KVSEL_PATH_GENERAL 2 /* general kernels: any supported dtype and head_dim */
+
 #define KVSEL_ACC_ADD 0       /* dst[b,h,:] += src[b,h,:] */
 #define KVSEL_ACC_HEAD_MEAN 1 /* dst[b,0,:]  = mean over h of src[b,h,:] */
 
@@ -80,11 +84,19 @@ typedef struct kvsel_score_desc {
     float softmax_scale; /* > 0, or <= 0 for 1/sqrt(head_dim) */
     int64_t q_strides[4];
     int64_t k_strides[4];
+    int32_t path;        /* KVSEL_PATH_AUTO (0), _STREAM or _GENERAL: which kernels score */
+    int32_t reserved;    /* must be 0 */
 } kvsel_score_desc_t;
 
 /* Device workspace, in bytes, that kvsel_score needs for `desc` (0 on an
  * invalid descriptor). */
 size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc);
+
+/* The scoring kernels a call with `desc` runs: KVSEL_PATH_STREAM or
+ * KVSEL_PATH_GENERAL (what KVSEL_PATH_AUTO resolves to), or -1 when the
+ * descriptor is invalid or asks for the streaming kernels on a shape they do
+ * not take (kvsel_score then returns KVSEL_ERR_UNSUPPORTED). Host only. */
+int32_t kvsel_score_path(const kvsel_score_desc_t* desc);
 
 /*
  * Saliency scores of every prefix key (FastKV section 2A; StructKV section 1).
@@ -99,13 +111,13 @@ size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc);
  *         window row.
  * workspace  device, >= kvsel_score_workspace_bytes(desc) bytes, 256-byte
  *         aligned; its content is scratch between calls.
- * Paths: bf16 with head_dim 64/128 and w <= 256 streams K in two passes
- * (when G*w > 256 the group's query heads are streamed in head groups of at
- * most 256 rows, each reading the keys); other shapes take a general
- * two-pass path. The environment variable
- * KVSEL_SCORE_PATH=resident (register-resident, single K read) or =general
- * forces another path where it applies; every path computes the same result
- * to the stated tolerance.
+ * Paths (desc->path): KVSEL_PATH_AUTO streams K in two passes for bf16 with
+ * head_dim 64/128 and w <= 256 (when G*w > 256 the group's query heads are
+ * streamed in head groups of at most 256 rows, each reading the keys) and
+ * takes the general two-pass kernels for other shapes; KVSEL_PATH_STREAM or
+ * _GENERAL asks for one of them explicitly (the streaming choice on a shape
+ * it does not take returns UNSUPPORTED). Both compute the same result to the
+ * stated tolerance.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,

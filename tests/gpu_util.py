@@ -52,16 +52,30 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
+PATHS = {"auto": K.KVSEL_PATH_AUTO, "stream": K.KVSEL_PATH_STREAM, "general": K.KVSEL_PATH_GENERAL}
+
+
+def stream_eligible(wl) -> bool:
+    """Whether the streaming kernels take this shape (what AUTO picks)."""
+    return wl.dtype == "bf16" and wl.head_dim in (64, 128) and wl.window <= 256
+
+
 def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None, lse_in=None, pool_type=0,
-            n_sink=0):
+            n_sink=0, path="auto"):
     """The path as the benchmark runs it: one kvsel_score call over every
     layer, the per-KV-head select, the K/V gather over every layer, and (with
     a TSP budget) head mean, token-set select and hidden gather. With
     ``lse_in`` ([L, B, Hq, w] natural-log LSE) the scoring call is
     kvsel_score_lse instead. ``pool_type`` picks the pool (K.KVSEL_POOL_*),
-    ``n_sink`` the protected first positions of both selections."""
+    ``n_sink`` the protected first positions of both selections. ``path``
+    ("auto", "stream", "general") picks the scoring kernels; the library's
+    own report of the kernels it runs must match."""
     q = to_dev(inp["q"], wl.dtype)
     k = to_dev(inp["k"], wl.dtype)
+    desc = K.score_desc(q, k, wl.window, wl.pool_kernel, 0.0, pool_type, PATHS[path])
+    expect = K.KVSEL_PATH_STREAM if (path == "stream" or (path == "auto" and stream_eligible(wl))) else \
+        K.KVSEL_PATH_GENERAL
+    assert K.kvsel_score_path(desc) == expect, (path, K.kvsel_score_path(desc))
     L, B, Hq, w, d = inp["q"].shape
     out = {}
     lse = torch.full((L, B, Hq, w), float("nan"), device=device()) if with_lse and lse_in is None else None
@@ -70,12 +84,12 @@ def run_gpu(wl, inp, *, with_lse=True, with_gather=True, accumulate_into=None, l
     else:
         scores = torch.full((B, wl.n_kv_heads, wl.n_keys - wl.window), float("nan"), device=device())
     if lse_in is None:
-        K.kvsel_score(q, k, scores, window=wl.window, pool_kernel=wl.pool_kernel, pool_type=pool_type,
-                      accumulate=accumulate_into is not None, lse_out=lse)
+        K.kvsel_score(q, k, scores, window=wl.window, accumulate=accumulate_into is not None, lse_out=lse,
+                      desc=desc)
     else:
         lse_dev = torch.from_numpy(np.ascontiguousarray(lse_in, dtype=np.float32)).to(device())
-        K.kvsel_score_lse(q, k, lse_dev, scores, window=wl.window, pool_kernel=wl.pool_kernel,
-                          pool_type=pool_type, accumulate=accumulate_into is not None)
+        K.kvsel_score_lse(q, k, lse_dev, scores, window=wl.window, accumulate=accumulate_into is not None,
+                          desc=desc)
     idx = K.kvsel_topk(scores, n_keys=wl.n_keys, window=wl.window, budget=wl.kv_budget, n_sink=n_sink)
     out["scores"] = scores.cpu().numpy()
     out["idx"] = idx.cpu().numpy()

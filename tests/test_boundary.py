@@ -47,9 +47,10 @@ def test_struct_layout_matches_header():
 #include <stddef.h>
 #include "kvsel.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(kvsel_score_desc_t), offsetof(kvsel_score_desc_t, n_keys),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(kvsel_score_desc_t), offsetof(kvsel_score_desc_t, n_keys),
          offsetof(kvsel_score_desc_t, pool_kernel), offsetof(kvsel_score_desc_t, softmax_scale),
-         offsetof(kvsel_score_desc_t, q_strides), offsetof(kvsel_score_desc_t, k_strides));
+         offsetof(kvsel_score_desc_t, q_strides), offsetof(kvsel_score_desc_t, k_strides),
+         offsetof(kvsel_score_desc_t, path), offsetof(kvsel_score_desc_t, reserved));
   return 0;
 }
 """
@@ -61,7 +62,7 @@ int main(void) {
         got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
     D = kvsel.ScoreDesc
     assert got == [ctypes.sizeof(D), D.n_keys.offset, D.pool_kernel.offset, D.softmax_scale.offset,
-                   D.q_strides.offset, D.k_strides.offset]
+                   D.q_strides.offset, D.k_strides.offset, D.path.offset, D.reserved.offset]
 
 
 def test_status_strings(lib):
@@ -100,12 +101,39 @@ FAKE = 1 << 32  # a 256-byte aligned address that is never dereferenced
     ("softmax_scale", float("inf"), 1), ("softmax_scale", float("nan"), 1),
     ("head_dim", 96, 2), ("dtype", 7, 2), ("pool_type", 2, 2),
     ("k_strides", [0, 0, 1024 * 128, 127], 1), ("q_strides", [0, 0, -128, 128], 1),
+    ("path", 3, 1), ("path", -1, 1), ("reserved", 1, 1),
 ])
 def test_score_rejects_bad_descriptor(lib, field, value, status):
     d = good_desc(**{field: value})
     assert lib.kvsel_score_workspace_bytes(ctypes.byref(d)) == 0
     st = lib.kvsel_score(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, FAKE, 1 << 40, None)
     assert st == status
+
+
+def test_score_path_field(lib):
+    """The explicit path field: AUTO resolves to the streaming kernels for a
+    bf16 head_dim-128 shape and to the general ones for fp32, head_dim 64
+    with w > 256 is general only, and an explicit streaming choice on a shape
+    it does not take resolves to -1 and is refused with UNSUPPORTED before
+    any launch."""
+    S, G, A = kvsel.KVSEL_PATH_STREAM, kvsel.KVSEL_PATH_GENERAL, kvsel.KVSEL_PATH_AUTO
+    assert lib.kvsel_score_path(ctypes.byref(good_desc())) == S
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(path=S))) == S
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(path=G))) == G
+    f32 = dict(dtype=kvsel.KVSEL_DTYPE_F32)
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(**f32))) == G
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(path=G, **f32))) == G
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(path=S, **f32))) == -1
+    wide = dict(head_dim=64, window=300, n_keys=1024, q_strides=[4 * 300 * 64, 4 * 300 * 64, 300 * 64, 64],
+                k_strides=[2 * 1024 * 64, 2 * 1024 * 64, 1024 * 64, 64])
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(path=A, **wide))) == G
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(path=S, **wide))) == -1
+    assert lib.kvsel_score_path(ctypes.byref(good_desc(path=7))) == -1
+    assert lib.kvsel_score_path(None) == -1
+    d = good_desc(path=S, **f32)
+    need = lib.kvsel_score_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert lib.kvsel_score(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None, FAKE, need, None) == 2
 
 
 def test_score_rejects_pointers_and_workspace(lib):

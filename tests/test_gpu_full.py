@@ -33,9 +33,9 @@ def inputs_and_oracle(name):
     return _CACHE[name]
 
 
-@pytest.mark.parametrize("path", ["stream", "resident", "given_lse"])
+@pytest.mark.parametrize("path", ["auto", "given_lse"])
 @pytest.mark.parametrize("name", ["llama8b_32k_tsp", "batched_8x32k_ar1", "qwen7b_512k", "structkv_128k_16l"])
-def test_full_workload(path, name, monkeypatch):
+def test_full_workload(path, name):
     wl, inp, ref = inputs_and_oracle(name)
     t0 = time.time()
     say(f"case {name} [{path}]: running the HIP path")
@@ -44,8 +44,7 @@ def test_full_workload(path, name, monkeypatch):
         # oracle's scores are the reference (they were computed with that LSE)
         gpu = run_gpu(wl, inp, lse_in=ref["lse"].astype(np.float32))
     else:
-        monkeypatch.setenv("KVSEL_SCORE_PATH", path)
-        gpu = run_gpu(wl, inp)
+        gpu = run_gpu(wl, inp, path=path)
     say(f"case {name} [{path}]: comparing ({time.time() - t0:.1f}s)")
     check_all(wl, inp, gpu, ref)
     say(f"case {name} [{path}]: done ({time.time() - t0:.1f}s)")

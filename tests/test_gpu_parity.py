@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from gpu_util import (assert_gather, assert_scores_close, assert_selection, check_all, device, oracle_for,
-                      run_gpu, say, to_dev)
+                      run_gpu, say, stream_eligible, to_dev)
 from token_selection_amd import kvsel as K
 from workloads import get_workload, make_inputs
 
@@ -48,39 +48,60 @@ RAGGED = [
 ]
 
 
-@pytest.mark.parametrize("path", ["stream", "resident", "general"])
+def _skip_if_not_streamable(wl, path):
+    if path == "stream" and not stream_eligible(wl):
+        pytest.skip("the streaming kernels do not take this shape (the explicit choice returns UNSUPPORTED, "
+                    "checked in test_stream_path_refuses_other_shapes)")
+
+
+@pytest.mark.parametrize("path", ["auto", "stream", "general"])
 @pytest.mark.parametrize("case", RAGGED, ids=lambda c: "-".join(map(str, c)))
-def test_ragged_shapes(case, path, monkeypatch):
-    """Every scoring path the library has (where a shape is outside a path's
-    range the library takes the next one, so those cases repeat a path)."""
+def test_ragged_shapes(case, path):
+    """Every scoring path the library has, chosen explicitly through the
+    descriptor (the library's report of the kernels it runs is checked)."""
     dt, L, B, Hq, Hkv, d, N, w, pool, budget = case
-    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
     say("case ragged", case, path)
     wl = TINY.with_(name="ragged", wid=100 + RAGGED.index(case), dtype=dt, n_layers=L, batch=B, n_q_heads=Hq,
                     n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool, kv_budget=budget,
                     n_hubs=min(8, max(0, N - w - 1)))
+    _skip_if_not_streamable(wl, path)
     inp = make_inputs(wl)
-    gpu = run_gpu(wl, inp)
+    gpu = run_gpu(wl, inp, path=path)
     ref = oracle_for(wl, inp)
     check_all(wl, inp, gpu, ref)
+
+
+def test_stream_path_refuses_other_shapes():
+    """An explicit streaming choice on fp32 input is refused before any
+    launch, with UNSUPPORTED, and nothing is written."""
+    wl = TINY
+    inp = make_inputs(wl)
+    q, k = to_dev(inp["q"], "f32"), to_dev(inp["k"], "f32")
+    scores = torch.full((1, wl.n_kv_heads, wl.n_keys - wl.window), 7.0, device=device())
+    desc = K.score_desc(q, k, wl.window, wl.pool_kernel, path=K.KVSEL_PATH_STREAM)
+    assert K.kvsel_score_path(desc) == -1
+    with pytest.raises(K.KvselError) as e:
+        K.kvsel_score(q, k, scores, window=wl.window, desc=desc)
+    assert e.value.status == K.KVSEL_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((scores == 7.0).all())
 
 
 MAXPOOL_CASES = [RAGGED[0], RAGGED[1], RAGGED[6], RAGGED[7], RAGGED[9], RAGGED[10], RAGGED[3], RAGGED[12]]
 
 
-@pytest.mark.parametrize("path", ["stream", "resident", "general"])
+@pytest.mark.parametrize("path", ["auto", "general"])
 @pytest.mark.parametrize("case", MAXPOOL_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_max_pool(case, path, monkeypatch):
+def test_max_pool(case, path):
     """The max-pool variant on every scoring path: per-layer max over the pool
     window, then the layer sum (multi-layer cases check that order)."""
     dt, L, B, Hq, Hkv, d, N, w, pool, budget = case
-    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
     say("case max-pool", case, path)
     wl = TINY.with_(name="maxpool", wid=400 + MAXPOOL_CASES.index(case), dtype=dt, n_layers=L, batch=B,
                     n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool,
                     kv_budget=budget, n_hubs=min(8, max(0, N - w - 1)))
     inp = make_inputs(wl)
-    gpu = run_gpu(wl, inp, pool_type=K.KVSEL_POOL_MAX)
+    gpu = run_gpu(wl, inp, pool_type=K.KVSEL_POOL_MAX, path=path)
     ref = oracle_for(wl, inp, pool_type=K.KVSEL_POOL_MAX)
     check_all(wl, inp, gpu, ref)
 
@@ -272,14 +293,13 @@ def test_strided_query_view():
 LSE_CASES = [c for c in RAGGED if c[0] == "bf16"] + [RAGGED[8], RAGGED[9]]
 
 
-@pytest.mark.parametrize("path", ["stream", "general"])
+@pytest.mark.parametrize("path", ["auto", "general"])
 @pytest.mark.parametrize("case", LSE_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_scores_from_given_lse(case, path, monkeypatch):
+def test_scores_from_given_lse(case, path):
     """kvsel_score_lse (single pass, the window rows' LSE handed in) against the
     oracle given the same LSE: the true LSE (fp32-rounded) and one shifted per
     row by seeded offsets, so that the result is not the self-normalised one."""
     dt, L, B, Hq, Hkv, d, N, w, pool, budget = case
-    monkeypatch.setenv("KVSEL_SCORE_PATH", path)
     say("case given-lse", case, path)
     wl = TINY.with_(name="given_lse", wid=300 + LSE_CASES.index(case), dtype=dt, n_layers=L, batch=B,
                     n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool,
@@ -290,7 +310,7 @@ def test_scores_from_given_lse(case, path, monkeypatch):
     for lse in (ref0["lse"], ref0["lse"] + offs):
         lse32 = lse.astype(np.float32)
         ref = oracle_for(wl, inp, lse_in=lse32.astype(np.float64))
-        gpu = run_gpu(wl, inp, lse_in=lse32)
+        gpu = run_gpu(wl, inp, lse_in=lse32, path=path)
         check_all(wl, inp, gpu, ref)
 
 

@@ -5,8 +5,6 @@
 
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include <hip/hip_runtime.h>
 
@@ -36,6 +34,9 @@ kvsel_status_t validate_desc(const kvsel_score_desc_t* d) {
     if (d->dtype != KVSEL_DTYPE_F32 && d->dtype != KVSEL_DTYPE_BF16) return KVSEL_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
     if (d->pool_type != KVSEL_POOL_AVG && d->pool_type != KVSEL_POOL_MAX) return KVSEL_ERR_UNSUPPORTED;
+    if (d->path != KVSEL_PATH_AUTO && d->path != KVSEL_PATH_STREAM && d->path != KVSEL_PATH_GENERAL)
+        return KVSEL_ERR_INVALID_ARG;
+    if (d->reserved != 0) return KVSEL_ERR_INVALID_ARG;
     const int64_t e = d->dtype == KVSEL_DTYPE_F32 ? 4 : 2;
     for (int i = 0; i < 4; ++i)
         if ((d->q_strides[i] * e) % 16 != 0 || (d->k_strides[i] * e) % 16 != 0) return KVSEL_ERR_INVALID_ARG;
@@ -96,8 +97,7 @@ struct Plan {
     ScoreWs gen;               // general two-pass layout (any dtype)
     kvsel::StreamPlan stream;  // streaming bf16 layout (stream.ok when eligible)
     int T, Gs;                 // streaming head groups: T groups of at most Gs query heads per KV head
-    kvsel::KresPlan kres;      // register-resident bf16 layout (kres.ok when eligible)
-    size_t stream_total, kres_total, total;
+    size_t stream_total, total;
 };
 
 size_t raw_bytes(int64_t S, int64_t Np) { return ((size_t)S * Np * sizeof(float) + 255) & ~(size_t)255; }
@@ -121,7 +121,7 @@ void make_plan(const kvsel_score_desc_t* d, Plan& p) {
     p.gen = ws_layout(p.g);
     p.total = p.gen.total;
     const int n_cu = device_cu_count();
-    p.stream_total = p.kres_total = 0;
+    p.stream_total = 0;
     head_groups(p.g, p.T, p.Gs);
     const int64_t S_groups = (int64_t)p.g.S * p.T;
     p.stream.ok = false;
@@ -130,22 +130,16 @@ void make_plan(const kvsel_score_desc_t* d, Plan& p) {
         p.stream_total = p.stream.raw_off + raw_bytes(S_groups, p.g.Np);
         if (p.stream_total > p.total) p.total = p.stream_total;
     }
-    if (kvsel::kres_plan(d->dtype, d->head_dim, p.g.R, p.g.N, p.g.S, n_cu, p.kres)) {
-        p.kres_total = p.kres.raw_off + raw_bytes(p.g);
-        if (p.kres_total > p.total) p.total = p.kres_total;
-    }
 }
 
-// Scoring path: KVSEL_SCORE_PATH = "stream", "resident" or "general" forces
-// one where it applies; by default the streaming path for bf16, else general.
-enum class Path { Stream, Resident, General };
-
-Path choose_path(const Plan& p) {
-    const char* env = getenv("KVSEL_SCORE_PATH");
-    if (env && strcmp(env, "resident") == 0 && p.kres.ok && kvsel::kres_fits(p.kres)) return Path::Resident;
-    if (env && strcmp(env, "general") == 0) return Path::General;
-    if (p.stream.ok) return Path::Stream;
-    return Path::General;
+// Scoring path of a call: the descriptor's explicit choice, or for
+// KVSEL_PATH_AUTO the streaming kernels wherever they apply (bf16, head_dim 64
+// or 128, w <= 256), else the general kernels. -1: an explicit streaming
+// choice on a shape the streaming kernels do not take.
+int resolve_path(const kvsel_score_desc_t* d, const Plan& p) {
+    if (d->path == KVSEL_PATH_GENERAL) return KVSEL_PATH_GENERAL;
+    if (d->path == KVSEL_PATH_STREAM) return p.stream.ok ? KVSEL_PATH_STREAM : -1;
+    return p.stream.ok ? KVSEL_PATH_STREAM : KVSEL_PATH_GENERAL;
 }
 
 kvsel_status_t from_hip(hipError_t e) { return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP; }
@@ -180,10 +174,11 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
     float* raw = nullptr;
     int raw_layers = g.L;  // slices of raw that the pool sums (layers, times head groups)
     bool done = false;
-    if (stats && !p.stream.ok) return KVSEL_ERR_UNSUPPORTED;  // the statistics ride on the streaming passes
-    Path path = stats ? Path::Stream : choose_path(p);
-    if (lse_in && path == Path::Resident) path = p.stream.ok ? Path::Stream : Path::General;
-    if (path == Path::Stream) {
+    const int path = resolve_path(desc, p);
+    if (path < 0) return KVSEL_ERR_UNSUPPORTED;
+    // the statistics ride on the streaming passes
+    if (stats && path != KVSEL_PATH_STREAM) return KVSEL_ERR_UNSUPPORTED;
+    if (path == KVSEL_PATH_STREAM) {
         kvsel::StreamArgs a;
         a.q = static_cast<const uint16_t*>(q_win);
         a.k = static_cast<const uint16_t*>(k);
@@ -236,46 +231,6 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         }
         done = true;
     }
-    if (path == Path::Resident) {
-        kvsel::KresArgs a;
-        a.q = static_cast<const uint16_t*>(q_win);
-        a.k = static_cast<const uint16_t*>(k);
-        for (int i = 0; i < 4; ++i) {
-            a.qs[i] = g.qs[i];
-            a.ks[i] = g.ks[i];
-        }
-        a.B = g.B;
-        a.Hq = g.Hq;
-        a.Hkv = g.Hkv;
-        a.G = g.G;
-        a.w = g.w;
-        a.R = g.R;
-        a.rbn = p.kres.rbn;
-        a.N = (int32_t)g.N;
-        a.Np = (int32_t)g.Np;
-        a.S = g.S;
-        a.team_wgs = p.kres.team_wgs;
-        a.n_teams = p.kres.n_teams;
-        a.n_act = p.kres.n_act;
-        a.wg_per_stream = p.kres.wg_per_stream;
-        a.c = g.c;
-        a.invG = g.invG;
-        a.part = reinterpret_cast<uint64_t*>(ws + p.kres.part_off);
-        a.lse2 = reinterpret_cast<float*>(ws + p.kres.lse2_off);
-        a.slots = reinterpret_cast<uint64_t*>(ws + p.kres.part_off);
-        a.n_slots = (int64_t)((p.kres.slots_end - p.kres.part_off) / sizeof(uint64_t));
-        a.abort_word = reinterpret_cast<uint32_t*>(ws + p.kres.abort_off);
-        a.turn = reinterpret_cast<uint32_t*>(ws + p.kres.turn_off);
-        a.raw = reinterpret_cast<float*>(ws + p.kres.raw_off);
-        a.lse_out = lse_out;
-        a.spin_limit = 100000000;  // 1 s of the 100 MHz wall clock
-        if (kvsel::launch_kres(p.kres, a, hs) == hipSuccess) {
-            raw = a.raw;
-            done = true;
-        } else {
-            (void)hipGetLastError();  // launch refused: use the general path
-        }
-    }
     if (!done) {
         g.part = reinterpret_cast<float2*>(ws + p.gen.part_off);
         g.lse2 = reinterpret_cast<float*>(ws + p.gen.lse2_off);
@@ -310,6 +265,13 @@ size_t kvsel_score_workspace_bytes(const kvsel_score_desc_t* desc) {
     Plan p;
     make_plan(desc, p);
     return p.total;
+}
+
+int32_t kvsel_score_path(const kvsel_score_desc_t* desc) {
+    if (validate_desc(desc) != KVSEL_OK) return -1;
+    Plan p;
+    make_plan(desc, p);
+    return resolve_path(desc, p);
 }
 
 kvsel_status_t kvsel_score(const kvsel_score_desc_t* desc, const void* q_win, const void* k, float* scores,

@@ -55,41 +55,6 @@ hipError_t launch_lse_from_input(const float* lse_in, float* lse2, int S, int st
 hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64_t Np, int pool_kernel, int pool_type,
                        int accumulate, hipStream_t stream);
 
-// Register-resident path (bf16): one cooperative launch reads K once.
-struct KresArgs {
-    const uint16_t* q;
-    const uint16_t* k;
-    int64_t qs[4];
-    int64_t ks[4];
-    int32_t B, Hq, Hkv, G, w, R, rbn;
-    int32_t N, Np, S;
-    int32_t team_wgs;       // work-groups that split one slab's keys
-    int32_t n_teams;        // teams per stream
-    int32_t n_act;          // work-groups of a team that hold keys
-    int32_t wg_per_stream;  // n_teams * team_wgs; the grid is two streams
-    float c, invG;
-    uint64_t* part;   // [S][team_wgs][rp] per-work-group (max, sum) bit pairs, log2 domain
-    float* lse2;      // [S][rp] row LSE, log2 domain (directly after part)
-    uint64_t* slots;  // part and lse2 as one span of n_slots 64-bit words (sentinel-filled)
-    int64_t n_slots;
-    uint32_t* abort_word;
-    uint32_t* turn;   // per-CU load-turn table (zero-filled before the launch)
-    float* raw;       // [S][Np]
-    float* lse_out;   // [L][B][Hq][w] or null
-    int64_t spin_limit;  // wall-clock ticks (100 MHz) a wait may last
-};
-
-struct KresPlan {
-    bool ok;
-    int head_dim;
-    int kb, team_wgs, n_teams, n_act, wg_per_stream, rbn, rbn_cap, rp;
-    size_t part_off, lse2_off, slots_end, abort_off, turn_off, raw_off, total;
-};
-
-bool kres_plan(int dtype, int head_dim, int R, int64_t N, int64_t S, int n_cu, KresPlan& plan);
-bool kres_fits(const KresPlan& plan);
-hipError_t launch_kres(const KresPlan& plan, KresArgs a, hipStream_t stream);
-
 // Streaming path (bf16): pass 1 partials, merge, pass 2, each streaming K.
 struct StreamArgs {
     const uint16_t* q;

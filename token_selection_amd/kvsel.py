@@ -30,9 +30,13 @@ KVSEL_POOL_AVG = 0
 KVSEL_POOL_MAX = 1
 KVSEL_ACC_ADD = 0
 KVSEL_ACC_HEAD_MEAN = 1
+KVSEL_PATH_AUTO = 0
+KVSEL_PATH_STREAM = 1
+KVSEL_PATH_GENERAL = 2
 
 EXPORTED = (
     "kvsel_score_workspace_bytes",
+    "kvsel_score_path",
     "kvsel_score",
     "kvsel_score_lse",
     "kvsel_score_stats",
@@ -74,6 +78,8 @@ class ScoreDesc(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("q_strides", ctypes.c_int64 * 4),
         ("k_strides", ctypes.c_int64 * 4),
+        ("path", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -95,6 +101,8 @@ def load_library() -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.kvsel_score_workspace_bytes.argtypes = [ctypes.POINTER(ScoreDesc)]
     lib.kvsel_score_workspace_bytes.restype = sz
+    lib.kvsel_score_path.argtypes = [ctypes.POINTER(ScoreDesc)]
+    lib.kvsel_score_path.restype = i32
     lib.kvsel_score.argtypes = [ctypes.POINTER(ScoreDesc), vp, vp, vp, i32, vp, vp, sz, vp]
     lib.kvsel_score.restype = i32
     lib.kvsel_score_lse.argtypes = [ctypes.POINTER(ScoreDesc), vp, vp, vp, vp, i32, vp, sz, vp]
@@ -184,7 +192,7 @@ def _as5(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def score_desc(q_win: torch.Tensor, k: torch.Tensor, window: int, pool_kernel: int = 7,
-               softmax_scale: float = 0.0, pool_type: int = 0) -> ScoreDesc:
+               softmax_scale: float = 0.0, pool_type: int = 0, path: int = KVSEL_PATH_AUTO) -> ScoreDesc:
     q5, k5 = _as5(q_win, "q_win"), _as5(k, "k")
     L, B, Hq, w, d = q5.shape
     Lk, Bk, Hkv, N, dk = k5.shape
@@ -203,6 +211,8 @@ def score_desc(q_win: torch.Tensor, k: torch.Tensor, window: int, pool_kernel: i
     for i in range(4):
         desc.q_strides[i] = q5.stride(i)
         desc.k_strides[i] = k5.stride(i)
+    desc.path = int(path)
+    desc.reserved = 0
     return desc
 
 
@@ -210,16 +220,25 @@ def kvsel_score_workspace_bytes(desc: ScoreDesc) -> int:
     return int(load_library().kvsel_score_workspace_bytes(ctypes.byref(desc)))
 
 
+def kvsel_score_path(desc: ScoreDesc) -> int:
+    """KVSEL_PATH_STREAM or KVSEL_PATH_GENERAL: the kernels a scoring call with
+    ``desc`` runs (-1: invalid, or the streaming kernels asked for a shape
+    they do not take)."""
+    return int(load_library().kvsel_score_path(ctypes.byref(desc)))
+
+
 def kvsel_score(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Tensor] = None, *, window: int,
                 pool_kernel: int = 7, accumulate: bool = False, lse_out: Optional[torch.Tensor] = None,
                 softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None,
-                desc: Optional[ScoreDesc] = None, pool_type: int = 0) -> torch.Tensor:
+                desc: Optional[ScoreDesc] = None, pool_type: int = 0, path: int = KVSEL_PATH_AUTO) -> torch.Tensor:
     """Saliency scores [B, Hkv, N - w] (fp32), summed over the L layers of the
     call (added to ``scores`` when ``accumulate``). ``q_win``: [L, B, Hq, w, d]
-    or [B, Hq, w, d]; ``k``: [L, B, Hkv, N, d] or [B, Hkv, N, d]; bf16 or fp32."""
+    or [B, Hq, w, d]; ``k``: [L, B, Hkv, N, d] or [B, Hkv, N, d]; bf16 or fp32.
+    ``path`` picks the scoring kernels (KVSEL_PATH_*), used when ``desc`` is
+    not given."""
     lib = load_library()
     if desc is None:
-        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type)
+        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type, path)
     B, Hkv, N, w = desc.batch, desc.n_kv_heads, desc.n_keys, desc.window
     dev = k.device
     if scores is None:
@@ -241,13 +260,14 @@ def kvsel_score(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Ten
 def kvsel_score_lse(q_win: torch.Tensor, k: torch.Tensor, lse_in: torch.Tensor,
                     scores: Optional[torch.Tensor] = None, *, window: int, pool_kernel: int = 7,
                     accumulate: bool = False, softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
-                    stream=None, desc: Optional[ScoreDesc] = None, pool_type: int = 0) -> torch.Tensor:
+                    stream=None, desc: Optional[ScoreDesc] = None, pool_type: int = 0,
+                    path: int = KVSEL_PATH_AUTO) -> torch.Tensor:
     """As kvsel_score, with the natural-log LSE of every window row handed in
     (``lse_in``: contiguous float32 [L, B, Hq, w]); only the second softmax
     pass runs."""
     lib = load_library()
     if desc is None:
-        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type)
+        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type, path)
     B, Hkv, N, w = desc.batch, desc.n_kv_heads, desc.n_keys, desc.window
     dev = k.device
     if scores is None:
@@ -269,13 +289,13 @@ def kvsel_score_lse(q_win: torch.Tensor, k: torch.Tensor, lse_in: torch.Tensor,
 def kvsel_score_stats(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Tensor] = None, *, window: int,
                       small_p: float, pool_kernel: int = 7, accumulate: bool = False, lse_out=None,
                       softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None,
-                      desc: Optional[ScoreDesc] = None, pool_type: int = 0):
+                      desc: Optional[ScoreDesc] = None, pool_type: int = 0, path: int = KVSEL_PATH_AUTO):
     """As kvsel_score, also returning every window row's attention entropy,
     sum of p^2 and count of keys with p < small_p ([L, B, Hq, w] each):
     (scores, entropy, sum_p2, n_below)."""
     lib = load_library()
     if desc is None:
-        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type)
+        desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type, path)
     L, B, Hq, Hkv, N, w = desc.n_layers, desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.n_keys, desc.window
     dev = k.device
     if scores is None:
