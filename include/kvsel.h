@@ -271,6 +271,10 @@ kvsel_status_t kvsel_topk_sinks(int32_t batch, int32_t rows, int64_t n_keys, int
  * chosen_out   device int32 [n_slabs][n_merge] or NULL: the merged A numbers,
  *              ascending.
  * n_merge must not exceed kvsel_csm_candidates(...). head_dim 64 or 128.
+ * Keys must be finite: a key with NaN or Inf has NaN similarities, so its A
+ * token may rank among the chosen with no partner (score -inf, match -1); such
+ * a token is dropped without merging (its row and degree leave the output).
+ * The output stays n_out rows and no access leaves the buffers.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  *
  * kvsel_csm_candidates: host-only; the number of A tokens that have a B

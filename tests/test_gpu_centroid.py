@@ -94,6 +94,33 @@ def run_csm(k_bits, v_bits, deg, chunk, ns, nr, nm):
             "match": mt.cpu().numpy(), "chosen": ch.cpu().numpy()}
 
 
+def test_csm_chosen_token_without_partner():
+    """A key with a NaN element gives its A token NaN similarities, so it has no
+    partner (score -inf, match -1). With n_merge equal to the candidate count
+    that token ranks in; the merge drops it instead of writing outside the
+    span's LDS. The finite slab of the same call matches the oracle in full,
+    and the other slab keeps n_out rows with the dropped token's degree gone."""
+    n, d, chunk, ns, nr = 200, 128, 16, 2, 6
+    wl = BATCHED.with_(name="csm_nan", wid=690, n_layers=1, batch=1, n_kv_heads=2, n_q_heads=2, head_dim=d,
+                       n_keys=n, window=1, kv_budget=1)
+    inp = make_inputs(wl)
+    kb = inp["k"].reshape(2, n, d).copy()
+    vb = inp["v"].reshape(2, n, d)
+    bad = ns + 3 * chunk + 4          # an A position (even offset in its chunk) of slab 1
+    kb[1, bad, 5] = 0x7FC0             # bf16 NaN
+    nm = oracle_candidates(n, chunk, ns, nr)
+    say("case csm nan key", n, chunk, nm)
+    gpu = run_csm(kb.reshape(1, 1, 2, n, d), vb.reshape(1, 1, 2, n, d), None, chunk, ns, nr, nm)
+    per = {key: gpu[key].reshape((2,) + gpu[key].shape[3:]) for key in gpu}
+    ai = (bad - ns) // 2               # A number of the NaN token
+    assert per["match"][1][ai] == -1 and np.isneginf(per["score"][1][ai])
+    assert ai in per["chosen"][1].tolist()
+    assert per["degree"][1].shape == (n - nm,)
+    assert int(per["degree"][1].sum()) == n - 1   # every token but the dropped one is counted once
+    check_csm_slab(kb[0], vb[0], np.ones(n, dtype=np.int64), chunk, ns, nr, nm,
+                   {key: per[key][0] for key in per}, 0)
+
+
 # (L, B, Hkv, n, d, chunk, n_sink, n_recent, rate)
 CSM_CASES = [
     (1, 1, 2, 1000, 128, 64, 4, 32, 0.25),

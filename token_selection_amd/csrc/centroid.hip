@@ -289,9 +289,14 @@ __global__ void __launch_bounds__(kMergeThreads) csm_merge_kernel(CsmGeom g, con
         const int64_t ai = (int64_t)slab * g.n_a + (int64_t)c * (g.C >> 1) + (o >> 1);
         const bool chosen = in && (o & 1) == 0 && flags[ai] != 0;
         const uint64_t surv = __ballot(in && !chosen);
-        // merges: a chosen A token marks its partner (same chunk, so inside the span)
+        // merges: a chosen A token marks its partner (same chunk, so inside the
+        // span). A chosen token without a partner (match -1: only with
+        // non-finite keys, whose similarities are NaN) is dropped unmerged.
         __builtin_amdgcn_wave_barrier();
-        if (chosen) atomicOr(&mem_s[match[ai] - span0], 1ull << t);
+        if (chosen) {
+            const int64_t off = (int64_t)match[ai] - span0;
+            if (off >= 0 && off < 64) atomicOr(&mem_s[off], 1ull << t);
+        }
         long long dst = -1;
         if (in && !chosen) {
             const uint64_t chunk_bits = (ci * g.C + g.C >= 64) ? ~0ull << (ci * g.C) : ((1ull << (ci * g.C + g.C)) - 1) & (~0ull << (ci * g.C));
