@@ -34,10 +34,11 @@ DECODE_SOURCES = "token_selection_amd/csrc/decode.hip"
 CSM_SOURCES = "token_selection_amd/csrc/centroid.hip+token_selection_amd/csrc/topk.hip"
 
 
-def recorded_traffic(kernel: str, sources: str):
-    """HBM bytes per launch of `kernel` from the rocprofv3 PMC summaries under
-    profiles/, if they were taken on the current sources of that kernel (the
-    sha256 of the '+'-joined files, read in order, matches); otherwise None."""
+def recorded_traffic(kernel: str, sources: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 PMC
+    summaries under profiles/, if they were taken on the current sources of
+    that kernel (the sha256 of the '+'-joined files, read in order, matches)
+    and on the same workload; otherwise None."""
     import hashlib
     import re
 
@@ -50,14 +51,24 @@ def recorded_traffic(kernel: str, sources: str):
             return None
         h.update(open(path, "rb").read())
     sha = h.hexdigest()
-    pat = re.compile(r"traffic: kernel=(\S+) source=(\S+) sha256=([0-9a-f]+) bytes_per_launch=(\d+)")
+    pat = re.compile(r"traffic: kernel=(\S+) workload=(\S+) source=(\S+) sha256=([0-9a-f]+) bytes_per_launch=(\d+)")
     for name in sorted(os.listdir(PROFILES)):
         if not name.endswith(".md"):
             continue
         for m in pat.finditer(open(os.path.join(PROFILES, name)).read()):
-            if m.group(1) == kernel and m.group(2) == sources and m.group(3) == sha:
-                return int(m.group(4))
+            if m.group(1) == kernel and m.group(2) == workload and m.group(3) == sources and m.group(4) == sha:
+                return int(m.group(5))
     return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _cores() -> int:
@@ -120,6 +131,11 @@ def main() -> int:
     ap.add_argument("--csm", action="store_true",
                     help="time one CentroidKV chunked-soft-matching round (kvsel_csm) on the batched 8 x 32K "
                          "workload instead of the selection path")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch every kernel from Python each step instead of replaying HIP graphs")
+    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
+                    help="write 1 GiB before every timed step (auto: when K is below 1 GiB, so that it cannot sit "
+                         "in the 256 MB memory-side cache from the previous step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -157,10 +173,13 @@ def main() -> int:
 
     def up(a):
         if wl.dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
+    hidden = None
+    if wl.tsp_budget is not None and inp.get("hidden") is not None:
+        hidden = torch.from_numpy(inp["hidden"].view(np.int16)).to(dev).view(torch.bfloat16).unsqueeze(1)
     B, Hkv, N, w = wl.batch, wl.n_kv_heads, wl.n_keys, wl.window
     scores = torch.empty((B, Hkv, N - w), dtype=torch.float32, device=dev)
     idx = torch.empty((B, Hkv, wl.kv_budget), dtype=torch.int32, device=dev)
@@ -168,62 +187,116 @@ def main() -> int:
     ws = torch.empty(max(1, K.kvsel_score_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     kc = torch.empty((wl.n_layers, B, Hkv, wl.kv_budget, wl.head_dim), dtype=k.dtype, device=dev)
     vc = torch.empty_like(kc)
-    stream = torch.cuda.current_stream(dev)
-
-    stages = ("score", "topk", "gather")
-
-    def mk():
-        return torch.cuda.Event(enable_timing=True)
+    tsp = None
+    if wl.tsp_budget is not None:
+        tsp = {"score": torch.empty((B, 1, N - w), dtype=torch.float32, device=dev),
+               "idx": torch.empty((B, 1, wl.tsp_budget), dtype=torch.int32, device=dev)}
+        if hidden is not None:
+            tsp["hidden"] = torch.empty((B, 1, wl.tsp_budget, hidden.shape[-1]), dtype=hidden.dtype, device=dev)
+    tk_ws = torch.empty(max(1, K.kvsel_topk_workspace_bytes(B, Hkv, N, w, wl.kv_budget)), dtype=torch.uint8,
+                        device=dev)
+    tsp_ws = None if tsp is None else torch.empty(
+        max(1, K.kvsel_topk_workspace_bytes(B, 1, N, w, wl.tsp_budget)), dtype=torch.uint8, device=dev)
 
     lse_in = None
     if args.lse_in:
         lse_in = torch.empty(tuple(q.shape[:4]), dtype=torch.float32, device=dev)
         K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc, lse_out=lse_in)
         torch.cuda.synchronize()
-
     small_p = 1.0 / N  # keys below the uniform share
+    stats = None
+    if args.stats:
+        L, Hq = wl.n_layers, wl.n_q_heads
+        stats = {"entropy": torch.empty((L, B, Hq, w), dtype=torch.float32, device=dev),
+                 "sum_p2": torch.empty((L, B, Hq, w), dtype=torch.float32, device=dev),
+                 "n_below": torch.empty((L, B, Hq, w), dtype=torch.int32, device=dev),
+                 "summary": torch.empty((L, 3), dtype=torch.float32, device=dev)}
 
-    def step(evs=None):
-        # evs: per-stage (start, end) events recorded on the launch stream
-        if evs:
-            evs["score"][0].record(stream)
-        if args.stats:
-            _, ent, sp2, nb = K.kvsel_score_stats(q, k, scores, window=w, pool_kernel=wl.pool_kernel,
-                                                  small_p=small_p, workspace=ws, desc=desc)
-            K.kvsel_layer_summary(ent, sp2, nb, n_keys=N)
+    # the stages of one step; every buffer is allocated above, so a stage is
+    # kernel launches only and can be captured in a HIP graph
+    def stage_score():
+        if stats is not None:
+            K.kvsel_score_stats(q, k, scores, window=w, pool_kernel=wl.pool_kernel, small_p=small_p, workspace=ws,
+                                desc=desc, out=(stats["entropy"], stats["sum_p2"], stats["n_below"]))
+            K.kvsel_layer_summary(stats["entropy"], stats["sum_p2"], stats["n_below"], n_keys=N,
+                                  out=stats["summary"])
         elif lse_in is None:
             K.kvsel_score(q, k, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
         else:
             K.kvsel_score_lse(q, k, lse_in, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
-        if evs:
-            evs["score"][1].record(stream)
-            evs["topk"][0].record(stream)
-        K.kvsel_topk(scores, n_keys=N, window=w, budget=wl.kv_budget, idx=idx)
-        if evs:
-            evs["topk"][1].record(stream)
-            evs["gather"][0].record(stream)
+
+    def stage_topk():
+        K.kvsel_topk(scores, n_keys=N, window=w, budget=wl.kv_budget, idx=idx, workspace=tk_ws)
+        if tsp is not None:
+            K.kvsel_accumulate(scores, tsp["score"], mode=K.KVSEL_ACC_HEAD_MEAN)
+            K.kvsel_topk(tsp["score"], n_keys=N, window=w, budget=wl.tsp_budget, idx=tsp["idx"], workspace=tsp_ws)
+
+    def stage_gather():
         K.kvsel_gather(k, idx, kc)
         K.kvsel_gather(v, idx, vc)
-        if evs:
-            evs["gather"][1].record(stream)
+        if tsp is not None and "hidden" in tsp:
+            K.kvsel_gather(hidden, tsp["idx"], tsp["hidden"])
 
+    stages = {"score": stage_score, "topk": stage_topk, "gather": stage_gather}
+
+    def step():
+        for fn in stages.values():
+            fn()
+
+    stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: K steps back to back, one event pair around all of them
-    # and one around each stage of each step, all on the launch stream
-    per_step = [{n: (mk(), mk()) for n in stages} for _ in range(args.steps)]
-    t_begin, t_end = mk(), mk()
+    # one HIP graph per stage and one for the whole step (kernel nodes only:
+    # the library launches no memset or copy)
+    graphs = {}
+    if args.graph:
+        side = torch.cuda.Stream(dev)
+        for name, fn in list(stages.items()) + [("step", step)]:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                fn()
+            graphs[name] = g
+        torch.cuda.synchronize()
+    launch = {name: (graphs[name].replay if args.graph else fn) for name, fn in list(stages.items()) + [("step", step)]}
+
+    # cache hygiene: a workload whose K fits or nearly fits the 256 MB memory-
+    # side cache gets a 1 GiB write before every timed step (outside the
+    # timing), so that no step starts with K resident from the previous one
+    k_bytes = wl.compulsory_bytes()["k_read"]
+    flush = args.flush == "on" or (args.flush == "auto" and k_bytes < (1 << 30))
+    fbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+
+    def mk():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed_runs(fn, reps):
+        """reps runs of fn, each between two events on the launch stream."""
+        evs = [(mk(), mk()) for _ in range(reps)]
+        for e0, e1 in evs:
+            if fbuf is not None:
+                fbuf.fill_(1)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    # timed region: exactly `steps` steps, synchronised on both sides
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        step(per_step[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    step_ms = timed_runs(launch["step"], args.steps)
     wall = time.perf_counter() - t_wall
-    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
-    stage_ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in per_step) / args.steps for n in stages}
+    # the stages timed on their own (same launch form), for the stage split
+    # and the roofline of the scoring call
+    stage_runs = {name: timed_runs(launch[name], args.steps) for name in stages}
+
+    def med(x):
+        y = sorted(x)
+        return y[len(y) // 2] if len(y) % 2 else 0.5 * (y[len(y) // 2 - 1] + y[len(y) // 2])
+
+    ms_per_step = sum(step_ms) / len(step_ms)
+    stage_ms = {n: med(x) for n, x in stage_runs.items()}
 
     cb = wl.compulsory_bytes()
     units = wl.units
@@ -231,6 +304,8 @@ def main() -> int:
     score_alg_bytes = cb["k_read"] + cb["q_read"] + wl.batch * wl.n_kv_heads * wl.n_prefix * 4
     achieved = score_alg_bytes / (stage_ms["score"] / 1e3) / 1e9
     whole_gbs = cb["total"] / (ms_per_step / 1e3) / 1e9
+    kernel_name = ("kvsel_score_stats" if args.stats else "kvsel_score" if lse_in is None else "kvsel_score_lse")
+    traffic = recorded_traffic(kernel_name, STATS_SOURCES if args.stats else SCORE_SOURCES, wl.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -238,6 +313,7 @@ def main() -> int:
         cpu = cpu_baseline(wl, inp, mode="stats" if args.stats else "lse-in" if lse_in is not None else "two-pass",
                            lse=None if lse_in is None else lse_in.cpu().numpy().astype(np.float64),
                            small_p=small_p)
+        cpu["cpu_model"] = cpu_model()
 
     line = {
         "metric": "keys scored+selected/sec and achieved HBM GB/s (% of peak), 128K ctx",
@@ -247,6 +323,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": med(step_ms),
+        "ms_per_step_min": min(step_ms),
+        "ms_per_step_max": max(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -254,26 +333,24 @@ def main() -> int:
         "data": "synthetic (seeded; no dataset or weights)",
         "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "n_keys": wl.n_keys, "window": wl.window,
-                   "pool": wl.pool_kernel, "kv_budget": wl.kv_budget,
+                   "pool": wl.pool_kernel, "kv_budget": wl.kv_budget, "tsp_budget": wl.tsp_budget,
                    "lse": "computed (two passes)" if lse_in is None else "handed in (one pass)",
-                   "pivot_stats": bool(args.stats)},
+                   "pivot_stats": bool(args.stats), "launch": "hip graph" if args.graph else "eager",
+                   "cache_flush_between_steps": bool(flush)},
         "hbm_gbs_whole_path": whole_gbs,
         "hbm_frac_whole_path": whole_gbs / HBM_PEAK_GBS,
         "stage_ms": stage_ms,
-        # dominant launch group: the scoring call (kvsel_score: stream_kernel
-        # pass 1, the LSE merge, stream_kernel pass 2 and the pool, 89% of the
-        # step's kernel time; with --lse-in kvsel_score_lse: the LSE copy,
-        # pass 2 and the pool), timed with HIP events on its launch stream;
-        # algorithmic bytes = K read once + Q + final scores
+        # dominant launch group: the scoring call, timed with HIP events on its
+        # launch stream (median of `steps` runs); algorithmic bytes = K read
+        # once + Q + final scores
         "roofline": {"bound": "hbm",
                      "kernel": ("kvsel_score_stats (stream_kernel pass 1 + merge + pass 2 + count + pool + "
                                 "layer summary)" if args.stats else
                                 "kvsel_score (stream_kernel pass 1 + merge + pass 2 + pool)" if lse_in is None
                                 else "kvsel_score_lse (stream_kernel pass 2 + pool)"),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (recorded_traffic("kvsel_score_stats", STATS_SOURCES) if args.stats else
-                                 recorded_traffic("kvsel_score" if lse_in is None else "kvsel_score_lse",
-                                                  SCORE_SOURCES)),
+                     "traffic": traffic,
+                     "traffic_gbs": None if traffic is None else traffic / (stage_ms["score"] / 1e3) / 1e9,
                      "algorithmic_bytes": score_alg_bytes},
         "cpu_baseline": cpu,
         "wall_s_timed": wall,

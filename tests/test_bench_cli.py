@@ -1,10 +1,12 @@
-"""bench.py's command-line contract, on the CPU: it runs on one GPU only and
-says so for --gpus N > 1, and it refuses conflicting modes; both exits happen
-before any GPU work."""
+"""bench.py's command-line contract: it runs on one GPU only and says so for
+--gpus N > 1, and it refuses conflicting modes, both before any GPU work (CPU
+tests); on a GPU, its JSON line carries the report keys."""
 
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -25,3 +27,27 @@ def test_conflicting_modes_are_refused():
     r = run("--stats", "--lse-in")
     assert r.returncode == 2
     assert "separate modes" in r.stderr
+
+
+@pytest.mark.gpu
+def test_bench_line_carries_the_report_keys():
+    """One bench line on the small fp32 workload: the spread of the step
+    times, the launch form, the cache-flush flag, the roofline object and the
+    CPU baseline with its core count and CPU model."""
+    import json
+
+    r = run("--workload", "tiny_f32_2k", "--steps", "5", "--warmup", "2")
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "ms_per_step", "ms_per_step_median", "ms_per_step_min",
+                "ms_per_step_max", "stage_ms", "roofline", "cpu_baseline", "config"):
+        assert key in line, key
+    assert line["ms_per_step_min"] <= line["ms_per_step_median"] <= line["ms_per_step_max"]
+    assert line["config"]["workload"] == "tiny_f32_2k"
+    assert line["config"]["launch"] == "hip graph"
+    assert line["config"]["cache_flush_between_steps"] is True   # 1 MiB of K
+    roof = line["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    cpu = line["cpu_baseline"]
+    assert cpu["cores"] >= 1 and cpu["kind"] == "oracle" and isinstance(cpu["cpu_model"], str)

@@ -230,16 +230,20 @@ def test_exact_ties_follow_tie_break():
         assert_scores_close(gpu["scores"], ref["scores"])
 
 
-def test_large_logits_are_stable():
-    """Keys x 100 push logits to several hundred: the two-pass softmax must
-    subtract row maxima (fp32 exp overflows past 88)."""
-    wl = TINY.with_(name="big", wid=160, dtype="bf16", head_dim=128, k_mult=100.0, n_keys=3000, window=16,
+@pytest.mark.parametrize("path", ["auto", "general"])
+@pytest.mark.parametrize("k_mult,lse_floor", [(100.0, 300.0), (300.0, 900.0)])
+def test_large_logits_are_stable(k_mult, lse_floor, path):
+    """Keys x 100 push logits to several hundred, keys x 300 to about +-1000:
+    the two-pass softmax must subtract row maxima (fp32 exp overflows past
+    88), so the first-logit reference of pass 1 falls back to the row maximum
+    and every LSE still matches the oracle's."""
+    wl = TINY.with_(name="big", wid=160, dtype="bf16", head_dim=128, k_mult=k_mult, n_keys=3000, window=16,
                     kv_budget=200, n_hubs=0, hub_mode=None)
-    say("case large logits")
+    say("case large logits", k_mult, path)
     inp = make_inputs(wl)
-    gpu = run_gpu(wl, inp)
     ref = oracle_for(wl, inp)
-    assert np.abs(ref["lse"]).max() > 300
+    assert np.abs(ref["lse"]).max() > lse_floor  # the premise: logits of the stated size
+    gpu = run_gpu(wl, inp, path=path)
     check_all(wl, inp, gpu, ref)
 
 

@@ -289,10 +289,12 @@ def kvsel_score_lse(q_win: torch.Tensor, k: torch.Tensor, lse_in: torch.Tensor,
 def kvsel_score_stats(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Tensor] = None, *, window: int,
                       small_p: float, pool_kernel: int = 7, accumulate: bool = False, lse_out=None,
                       softmax_scale: float = 0.0, workspace: Optional[torch.Tensor] = None, stream=None,
-                      desc: Optional[ScoreDesc] = None, pool_type: int = 0, path: int = KVSEL_PATH_AUTO):
+                      desc: Optional[ScoreDesc] = None, pool_type: int = 0, path: int = KVSEL_PATH_AUTO,
+                      out=None):
     """As kvsel_score, also returning every window row's attention entropy,
     sum of p^2 and count of keys with p < small_p ([L, B, Hq, w] each):
-    (scores, entropy, sum_p2, n_below)."""
+    (scores, entropy, sum_p2, n_below). ``out`` = (entropy, sum_p2, n_below)
+    preallocated (float32, float32, int32 [L, B, Hq, w], contiguous)."""
     lib = load_library()
     if desc is None:
         desc = score_desc(q_win, k, window, pool_kernel, softmax_scale, pool_type, path)
@@ -305,9 +307,15 @@ def kvsel_score_stats(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[tor
     if lse_out is not None and (lse_out.dtype != torch.float32 or not lse_out.is_contiguous() or
                                 lse_out.numel() != L * B * Hq * w):
         raise ValueError("lse_out must be a contiguous float32 [L, B, Hq, w] tensor")
-    entropy = torch.empty((L, B, Hq, w), dtype=torch.float32, device=dev)
-    sum_p2 = torch.empty_like(entropy)
-    n_below = torch.empty((L, B, Hq, w), dtype=torch.int32, device=dev)
+    if out is None:
+        entropy = torch.empty((L, B, Hq, w), dtype=torch.float32, device=dev)
+        sum_p2 = torch.empty_like(entropy)
+        n_below = torch.empty((L, B, Hq, w), dtype=torch.int32, device=dev)
+    else:
+        entropy, sum_p2, n_below = out
+        for t, dt in ((entropy, torch.float32), (sum_p2, torch.float32), (n_below, torch.int32)):
+            if tuple(t.shape) != (L, B, Hq, w) or t.dtype != dt or not t.is_contiguous():
+                raise ValueError("out must be contiguous [L, B, Hq, w] tensors (float32, float32, int32)")
     need = int(lib.kvsel_score_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -319,7 +327,7 @@ def kvsel_score_stats(q_win: torch.Tensor, k: torch.Tensor, scores: Optional[tor
 
 
 def kvsel_layer_summary(entropy: torch.Tensor, sum_p2: torch.Tensor, n_below: torch.Tensor, *, n_keys: int,
-                        stream=None) -> torch.Tensor:
+                        stream=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-layer means [L, 3] (entropy, sparsity, variance) of kvsel_score_stats'
     row statistics [L, B, Hq, w]."""
     lib = load_library()
@@ -327,7 +335,10 @@ def kvsel_layer_summary(entropy: torch.Tensor, sum_p2: torch.Tensor, n_below: to
         if t.dim() != 4 or t.dtype != dt or not t.is_contiguous() or t.shape != entropy.shape:
             raise ValueError("statistics must be contiguous [L, B, Hq, w] tensors (float32, float32, int32)")
     L, B, Hq, w = entropy.shape
-    out = torch.empty((L, 3), dtype=torch.float32, device=entropy.device)
+    if out is None:
+        out = torch.empty((L, 3), dtype=torch.float32, device=entropy.device)
+    if tuple(out.shape) != (L, 3) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [L, 3] tensor")
     _check(lib.kvsel_layer_summary(L, B * Hq * w, w, n_keys, _ptr(entropy), _ptr(sum_p2), _ptr(n_below), _ptr(out),
                                    _stream(entropy.device, stream)), "kvsel_layer_summary")
     return out
