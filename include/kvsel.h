@@ -48,6 +48,7 @@ typedef int32_t kvsel_status_t;
 #define KVSEL_ERR_UNSUPPORTED 2 /* valid but not implemented: head_dim, dtype, pool type */
 #define KVSEL_ERR_WORKSPACE 3   /* workspace missing or smaller than the queried size */
 #define KVSEL_ERR_HIP 4         /* the HIP runtime reported a launch error */
+#define KVSEL_ERR_TOO_LARGE 5   /* more scratch than kvsel_topk_noalloc holds (KVSEL_TOPK_NOALLOC_MAX_BYTES) */
 
 #define KVSEL_DTYPE_F32 0  /* IEEE binary32 */
 #define KVSEL_DTYPE_BF16 1 /* bfloat16 (upper half of a binary32) */
@@ -240,6 +241,28 @@ kvsel_status_t kvsel_topk(int32_t batch, int32_t rows, int64_t n_keys, int32_t w
 kvsel_status_t kvsel_topk_sinks(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
                                 int32_t n_sink, const float* scores, int32_t* idx, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kvsel_topk_sinks without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments (minus the workspace),
+ * result and errors as kvsel_topk_sinks (n_sink = 0 is kvsel_topk).
+ *
+ * Its scratch (digit histograms, per-pass states, per-chunk counts) is a
+ * static device array of KVSEL_TOPK_NOALLOC_MAX_BYTES bytes (16 MiB), one
+ * copy per GPU, held until the process ends; the call allocates nothing. A
+ * problem whose scratch, kvsel_topk_workspace_bytes(batch, rows, n_keys,
+ * window, budget), exceeds that returns KVSEL_ERR_TOO_LARGE before any launch
+ * (about 680 selection rows at 131072 keys). Every call on a GPU shares that
+ * GPU's array: calls that can overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller; calls on one stream are
+ * ordered. The kernels clear what must start at zero, so a call never sees
+ * the previous call's contents. The first call on each device looks up the
+ * array's device address (hipGetSymbolAddress, no allocation).
+ */
+#define KVSEL_TOPK_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+kvsel_status_t kvsel_topk_noalloc(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
+                                  int32_t n_sink, const float* scores, int32_t* idx, void* stream);
 
 /*
  * CentroidKV chunked soft matching, one clustering round (page "Technische

@@ -66,7 +66,7 @@ int main(void) {
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert kvsel.status_string(code).startswith("KVSEL")
     assert "unknown" in kvsel.status_string(99)
     assert "gfx950" in kvsel.version()
@@ -175,6 +175,20 @@ def test_topk_sinks_rejects(lib, n_sink):
 def test_max_pool_accepted(lib):
     d = good_desc(pool_type=kvsel.KVSEL_POOL_MAX)
     assert lib.kvsel_score_workspace_bytes(ctypes.byref(d)) > 0
+
+
+def test_topk_noalloc_rejects(lib):
+    """The no-allocation top-k validates like kvsel_topk_sinks, and refuses a
+    problem whose scratch exceeds its static array with TOO_LARGE, before any
+    launch."""
+    assert lib.kvsel_topk_noalloc(1, 2, 1000, 8, 4, 0, FAKE, FAKE, None) == 1        # budget < window
+    assert lib.kvsel_topk_noalloc(1, 2, 1000, 8, 100, 93, FAKE, FAKE, None) == 1     # too many sinks
+    assert lib.kvsel_topk_noalloc(1, 2, 1000, 8, 100, 0, FAKE, None, None) == 1      # no idx
+    assert lib.kvsel_topk_noalloc(0, 2, 1000, 8, 100, 0, FAKE, FAKE, None) == 1
+    rows, n = 4000, 1 << 20
+    assert lib.kvsel_topk_workspace_bytes(1, rows, n, 8, 100) > kvsel.KVSEL_TOPK_NOALLOC_MAX_BYTES
+    assert lib.kvsel_topk_noalloc(1, rows, n, 8, 100, 0, FAKE, FAKE, None) == kvsel.KVSEL_ERR_TOO_LARGE
+    assert "no-allocation" in kvsel.status_string(kvsel.KVSEL_ERR_TOO_LARGE)
 
 
 def test_topk_rejects_null(lib):

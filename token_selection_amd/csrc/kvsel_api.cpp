@@ -254,6 +254,8 @@ const char* kvsel_status_string(kvsel_status_t status) {
         case KVSEL_ERR_UNSUPPORTED: return "KVSEL_ERR_UNSUPPORTED: unsupported head_dim, dtype or pool type";
         case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE: workspace missing or too small";
         case KVSEL_ERR_HIP: return "KVSEL_ERR_HIP: HIP runtime error";
+        case KVSEL_ERR_TOO_LARGE:
+            return "KVSEL_ERR_TOO_LARGE: the problem needs more scratch than the no-allocation entry point holds";
         default: return "KVSEL: unknown status";
     }
 }
@@ -346,6 +348,22 @@ kvsel_status_t kvsel_topk_sinks(int32_t batch, int32_t rows, int64_t n_keys, int
     const size_t need = kvsel::topk_workspace_bytes(batch * rows, n_keys - window);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVSEL_ERR_WORKSPACE;
     return from_hip(kvsel::launch_topk(batch * rows, n_keys, window, budget, n_sink, scores, idx, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+static_assert(KVSEL_TOPK_NOALLOC_MAX_BYTES == kvsel::kTopkScratchBytes, "the header states the scratch size");
+
+kvsel_status_t kvsel_topk_noalloc(int32_t batch, int32_t rows, int64_t n_keys, int32_t window, int32_t budget,
+                                  int32_t n_sink, const float* scores, int32_t* idx, void* stream) {
+    if (batch < 1 || rows < 1 || (int64_t)batch * rows > 65535) return KVSEL_ERR_INVALID_ARG;
+    if (window < 1 || budget < window || n_keys < budget || n_keys >= kMaxKeys) return KVSEL_ERR_INVALID_ARG;
+    if (n_sink < 0 || n_sink > budget - window) return KVSEL_ERR_INVALID_ARG;
+    if (!idx || (n_keys > window && !scores)) return KVSEL_ERR_INVALID_ARG;
+    if (kvsel::topk_workspace_bytes(batch * rows, n_keys - window) > kvsel::kTopkScratchBytes)
+        return KVSEL_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if (kvsel::topk_scratch(&ws) != hipSuccess) return KVSEL_ERR_HIP;
+    return from_hip(kvsel::launch_topk(batch * rows, n_keys, window, budget, n_sink, scores, idx, ws,
                                        static_cast<hipStream_t>(stream)));
 }
 

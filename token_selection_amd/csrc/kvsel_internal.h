@@ -106,6 +106,10 @@ hipError_t launch_layer_summary(int32_t L, int32_t rows, int32_t w, int64_t N, c
                                 const float* sum_p2, const int32_t* n_below, float* summary, hipStream_t stream);
 
 size_t topk_workspace_bytes(int32_t rows, int64_t n_prefix);
+// The no-allocation top-k's static scratch: its size, and its device address
+// on the current device (looked up once per device).
+constexpr size_t kTopkScratchBytes = (size_t)16 << 20;
+hipError_t topk_scratch(void** out);
 hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, int32_t n_sink,
                        const float* scores, int32_t* idx, void* workspace, hipStream_t stream);
 

@@ -27,7 +27,18 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kvsel_internal.h"
+
+// Scratch of kvsel_topk_noalloc: the histograms, per-pass states and chunk
+// counts of one call, in a static device array (one copy per GPU, held until
+// the process ends). Host code must not pass `scratch` itself to a kernel: its
+// name is a host-side stand-in, so the device address is looked up once per
+// device with hipGetSymbolAddress (topk_scratch below) and that is what the
+// kernels get.
+static __device__ __align__(256) unsigned char scratch[kvsel::kTopkScratchBytes];
 
 namespace kvsel {
 namespace {
@@ -340,6 +351,33 @@ void plan_chunks(int32_t rows, int64_t Np, int32_t& chunks, int64_t& chunk_len) 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t topk_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            // this device's copy of the array (the current device's address)
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 size_t topk_workspace_bytes(int32_t rows, int64_t Np) {
     int32_t chunks;

@@ -23,6 +23,8 @@ KVSEL_ERR_INVALID_ARG = 1
 KVSEL_ERR_UNSUPPORTED = 2
 KVSEL_ERR_WORKSPACE = 3
 KVSEL_ERR_HIP = 4
+KVSEL_ERR_TOO_LARGE = 5
+KVSEL_TOPK_NOALLOC_MAX_BYTES = 16 << 20
 
 KVSEL_DTYPE_F32 = 0
 KVSEL_DTYPE_BF16 = 1
@@ -46,6 +48,7 @@ EXPORTED = (
     "kvsel_topk_workspace_bytes",
     "kvsel_topk",
     "kvsel_topk_sinks",
+    "kvsel_topk_noalloc",
     "kvsel_gather",
     "kvsel_csm_candidates",
     "kvsel_csm_workspace_bytes",
@@ -123,6 +126,8 @@ def load_library() -> ctypes.CDLL:
     lib.kvsel_topk.restype = i32
     lib.kvsel_topk_sinks.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.kvsel_topk_sinks.restype = i32
+    lib.kvsel_topk_noalloc.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, vp]
+    lib.kvsel_topk_noalloc.restype = i32
     lib.kvsel_gather.argtypes = [i32, i32, i32, i32, i32, i64, i64, vp, ctypes.POINTER(ctypes.c_int64), vp, vp, vp]
     lib.kvsel_gather.restype = i32
     lib.kvsel_csm_candidates.argtypes = [i64, i32, i32, i32]
@@ -494,6 +499,24 @@ def kvsel_topk(scores: torch.Tensor, *, n_keys: int, window: int, budget: int, i
     else:
         _check(lib.kvsel_topk(B, rows, n_keys, window, budget, _ptr(scores), _ptr(idx), _ptr(workspace), ws_bytes,
                               _stream(scores.device, stream)), "kvsel_topk")
+    return idx
+
+
+def kvsel_topk_noalloc(scores: torch.Tensor, idx: torch.Tensor, *, n_keys: int, window: int, budget: int,
+                       n_sink: int = 0, stream=None) -> torch.Tensor:
+    """kvsel_topk without a workspace: the library's static per-GPU scratch
+    serves (calls that overlap on one GPU race). ``idx`` [B, rows, budget]
+    int32 must be given, so the call allocates nothing."""
+    lib = load_library()
+    if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B, rows, N - w] tensor")
+    B, rows, n_prefix = scores.shape
+    if n_prefix != n_keys - window:
+        raise ValueError("scores length must be n_keys - window")
+    if tuple(idx.shape) != (B, rows, budget) or idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 [B, rows, budget] tensor")
+    _check(lib.kvsel_topk_noalloc(B, rows, n_keys, window, budget, n_sink, _ptr(scores), _ptr(idx),
+                                  _stream(scores.device, stream)), "kvsel_topk_noalloc")
     return idx
 
 
