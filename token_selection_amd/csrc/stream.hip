@@ -160,14 +160,8 @@ __device__ __forceinline__ void load_chunk(Frag<D>& f, const StreamArgs& a, cons
         const int j = min(kbase + kb * 32 + col, a.N - 1);
         const uint16_t* row = kslab + (int64_t)j * a.ks[3] + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-#if defined(KVSEL_AB_NT)
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            f.v[kb][ks] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + ks * 16)));
-#else
+        for (int ks = 0; ks < D / 16; ++ks)
             f.v[kb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + ks * 16));
-#endif
-        }
     }
 }
 
@@ -264,13 +258,7 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
                 const int lim = row < rows ? a.Np + row % a.w : -1;
                 z = pass1_max<D, kKB, true>(f.v, qf, a.c, kbase, hf, lim, m);
             } else {
-#if defined(KVSEL_AB_PRIO)
-                __builtin_amdgcn_s_setprio(KVSEL_AB_PRIO);
-#endif
                 z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
-#if defined(KVSEL_AB_PRIO)
-                __builtin_amdgcn_s_setprio(0);
-#endif
                 if (__any(!(z < kOverflow))) z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
             }
             merge(rs.m[0], rs.z[0], m, z);
@@ -340,14 +328,8 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
         }
         // lane holds key kbase + kb*32 + col and rows rb*32 + tile_row(v, hf)
         f32x16 x[kKB];
-#if defined(KVSEL_AB_PRIO)
-        __builtin_amdgcn_s_setprio(KVSEL_AB_PRIO);
-#endif
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb) x[kb] = logits<KS>(qf, f.v[kb]);
-#if defined(KVSEL_AB_PRIO)
-        __builtin_amdgcn_s_setprio(0);
-#endif
         if constexpr (!ST) {
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb) {
