@@ -29,6 +29,9 @@ def _topk_case(scores_np, n_keys, window, budget):
     (100, 4, 10, "rand"), (100, 4, 4, "rand"), (100, 4, 100, "rand"), (5000, 32, 600, "ties"),
     (70000, 64, 3277, "rand"), (70000, 64, 8000, "ties"), (20000, 8, 2048, "const"), (9000, 1, 9000, "ties"),
     (131072, 32, 4096, "rand"), (4097, 1, 4096, "rand"), (300000, 64, 8192, "zeros_and_ties"),
+    # around the one-launch limit of 4096 prefix keys per row (one work-group per row up to it)
+    (4096 + 8, 8, 1024, "rand"), (4096 + 9, 8, 1024, "rand"), (4096 + 8, 8, 4096 + 8, "ties"),
+    (4096 + 8, 8, 3000, "ties"), (33, 1, 2, "const"), (2048, 32, 256, "zeros_and_ties"), (4096 + 8, 8, 9, "const"),
 ])
 def test_topk_matches_oracle(n_keys, window, budget, kind):
     say("topk", n_keys, window, budget, kind)

@@ -58,7 +58,10 @@ void make_geom(const kvsel_score_desc_t* d, ScoreGeom& g, int& RB) {
     g.S = g.L * g.B * g.Hkv;
     g.N = d->n_keys;
     g.Np = d->n_keys - d->window;
+    // general path: halve the chunk until the grid has ~2 work-groups per
+    // compute unit (or the chunk reaches its minimum)
     g.chunk = kvsel::kScoreChunk;
+    while (g.chunk > kvsel::kScoreChunkMin && (int64_t)g.S * ((g.N + g.chunk - 1) / g.chunk) < 512) g.chunk >>= 1;
     g.n_chunks1 = (int32_t)((g.N + g.chunk - 1) / g.chunk);
     g.n_chunks2 = (int32_t)((g.Np + g.chunk - 1) / g.chunk);
     const double scale = d->softmax_scale > 0.f ? (double)d->softmax_scale : 1.0 / sqrt((double)d->head_dim);

@@ -35,7 +35,11 @@ struct ScoreWs {
     size_t part_off, lse2_off, raw_off, total;
 };
 
-constexpr int kScoreChunk = 1024;  // keys per work-group in both passes
+// Keys per work-group chunk of the general path: kScoreChunk, or a smaller
+// power of two (down to kScoreChunkMin) when the call has too few chunks to
+// give every compute unit a couple of work-groups.
+constexpr int kScoreChunk = 1024;
+constexpr int kScoreChunkMin = 64;
 
 int score_row_blocks(int dtype, int head_dim, int R);  // RB (row blocks of 16 per group)
 ScoreWs score_workspace_layout(int64_t S, int64_t n_chunks1, int64_t Rpad, int64_t Np);

@@ -140,8 +140,8 @@ __global__ __launch_bounds__(256) void lse_partial_kernel(ScoreGeom g) {
     const int lg = lane >> 4;
     const T* kslab = static_cast<const T*>(g.k) + id.l * g.ks[0] + id.b * g.ks[1] + id.kvh * g.ks[2];
     const T* qbase = static_cast<const T*>(g.q) + id.l * g.qs[0] + id.b * g.qs[1];
-    const int j0 = chunk * kScoreChunk;
-    const int j1 = (int)min<int64_t>(g.N, (int64_t)j0 + kScoreChunk);
+    const int j0 = chunk * g.chunk;
+    const int j1 = (int)min<int64_t>(g.N, (int64_t)j0 + g.chunk);
     const int Np = (int)g.Np;
     __shared__ float2 red[4][RB * 16];
 
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(ScoreGeom g) {
 template <typename T, int D, int RB>
 __global__ __launch_bounds__(256) void raw_score_kernel(ScoreGeom g) {
     using F = Frag<T, D>;
-    constexpr int NKB = kScoreChunk / 64;  // 16-key blocks per wave per chunk
+    constexpr int NKB = kScoreChunk / 64;  // 16-key blocks per wave in the largest chunk
     const int chunk = blockIdx.x;
     const int s = blockIdx.y;
     const SlabId id = slab_id(g, s);
@@ -275,8 +275,8 @@ __global__ __launch_bounds__(256) void raw_score_kernel(ScoreGeom g) {
     const int lg = lane >> 4;
     const T* kslab = static_cast<const T*>(g.k) + id.l * g.ks[0] + id.b * g.ks[1] + id.kvh * g.ks[2];
     const T* qbase = static_cast<const T*>(g.q) + id.l * g.qs[0] + id.b * g.qs[1];
-    const int j0 = chunk * kScoreChunk;
-    const int j1 = (int)min<int64_t>(g.Np, (int64_t)j0 + kScoreChunk);
+    const int j0 = chunk * g.chunk;
+    const int j1 = (int)min<int64_t>(g.Np, (int64_t)j0 + g.chunk);
     const float* lse2 = g.lse2 + (int64_t)s * g.Rpad;
 
     float cs[NKB];

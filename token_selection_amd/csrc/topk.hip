@@ -319,6 +319,120 @@ __global__ __launch_bounds__(kThreads) void topk_write_kernel(TopkGeom g) {
     }
 }
 
+// Rows of at most kRowMax prefix keys (the short rows of small problems,
+// where six launches would cost more than the work) take one work-group of
+// kRowThreads threads per row and a single launch: thread t holds the rank keys of the
+// row's positions [t*kRowPer, t*kRowPer + kRowPer) in registers, each wave
+// counts digits into its own LDS histogram (conflicts stay inside a wave), the
+// histograms are summed per digit and scanned from the highest digit down to
+// pick the digit of the k-th key, three times (11, 11, 10 bits); then each
+// thread counts its keys above T and equal to T, one block scan turns the
+// counts into output slots, and every thread writes its kept positions in
+// ascending order.
+constexpr int kRowThreads = 256;
+constexpr int kRowPer = 16;
+constexpr int kRowMax = kRowThreads * kRowPer;  // 4096
+constexpr int kRowWaves = kRowThreads / 64;
+
+// Exclusive scan of v over the block (kRowThreads threads); *total gets the sum.
+__device__ __forceinline__ uint32_t row_block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t incl = wave_inclusive_scan(v, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0u, all = 0u;
+#pragma unroll
+    for (int w2 = 0; w2 < kRowWaves; ++w2) {
+        const uint32_t t = wsum[w2];
+        before += w2 < wave ? t : 0u;
+        all += t;
+    }
+    __syncthreads();  // wsum is reused by the next scan
+    *total = all;
+    return before + incl - v;
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const uint32_t* __restrict__ scores, int32_t* idx,
+                                                               int64_t Np, int32_t w, int32_t budget, int32_t kk,
+                                                               int32_t n_sink) {
+    __shared__ uint32_t hist[kRowWaves][kBins];
+    __shared__ uint32_t wsum[kRowWaves];
+    __shared__ uint32_t res[2];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    int32_t* out = idx + row * (int64_t)budget;
+    for (int m = tid; m < w; m += kRowThreads) out[kk + m] = (int32_t)(Np + m);
+    if (kk == 0) return;
+    const uint32_t* x = scores + row * Np;
+    const int64_t first = (int64_t)tid * kRowPer;
+    uint32_t u[kRowPer];
+#pragma unroll
+    for (int k = 0; k < kRowPer; ++k) u[k] = first + k < Np ? rank_key(x, first + k, n_sink) : 0u;
+    uint32_t prefix = 0u, remaining = (uint32_t)kk;
+#pragma unroll 1
+    for (int pass = 0; pass < kPasses; ++pass) {
+        for (int i = tid; i < kRowWaves * kBins; i += kRowThreads) (&hist[0][0])[i] = 0u;
+        __syncthreads();
+        const uint32_t pm = prefix_mask(pass);
+        const int shift = digit_shift(pass);
+        const uint32_t dm = digit_mask(pass);
+#pragma unroll
+        for (int k = 0; k < kRowPer; ++k)
+            if (first + k < Np && (u[k] & pm) == prefix) atomicAdd(&hist[wave][(u[k] >> shift) & dm], 1u);
+        __syncthreads();
+        // thread t owns the kDig digits 2047 - kDig*t ... (highest first)
+        constexpr int kDig = kBins / kRowThreads;
+        uint32_t c[kDig];
+        uint32_t mine = 0u;
+#pragma unroll
+        for (int k = 0; k < kDig; ++k) {
+            const int d = kBins - 1 - (kDig * tid + k);
+            uint32_t sum = 0u;
+#pragma unroll
+            for (int w2 = 0; w2 < kRowWaves; ++w2) sum += hist[w2][d];
+            c[k] = sum;
+            mine += sum;
+        }
+        uint32_t tot;
+        uint32_t above = row_block_scan(mine, wsum, &tot);
+#pragma unroll
+        for (int k = 0; k < kDig; ++k) {
+            const int d = kBins - 1 - (kDig * tid + k);
+            if (above < remaining && above + c[k] >= remaining) {
+                res[0] = prefix | ((uint32_t)d << shift);
+                res[1] = remaining - above;
+            }
+            above += c[k];
+        }
+        __syncthreads();
+        prefix = res[0];
+        remaining = res[1];
+        __syncthreads();  // res and hist are rewritten by the next pass
+    }
+    // prefix is now the k-th key T; remaining is how many keys equal to T are kept
+    uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+    for (int k = 0; k < kRowPer; ++k) {
+        const bool in = first + k < Np;
+        gt += (in && u[k] > prefix) ? 1u : 0u;
+        eq += (in && u[k] == prefix) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t excl = row_block_scan((gt << 16) | eq, wsum, &tot);
+    uint32_t gt_before = excl >> 16, eq_before = excl & 0xFFFFu;
+#pragma unroll
+    for (int k = 0; k < kRowPer; ++k) {
+        if (first + k >= Np) break;
+        if (u[k] > prefix) {
+            out[gt_before + min(eq_before, remaining)] = (int32_t)(first + k);
+            ++gt_before;
+        } else if (u[k] == prefix) {
+            if (eq_before < remaining) out[gt_before + eq_before] = (int32_t)(first + k);
+            ++eq_before;
+        }
+    }
+}
+
 // Writes the window positions and zeroes the digit histograms (it runs first).
 __global__ __launch_bounds__(kThreads) void topk_window_kernel(int32_t* idx, int32_t rows, int64_t Np, int32_t w,
                                                                int32_t budget, uint32_t* hist) {
@@ -391,6 +505,14 @@ size_t topk_workspace_bytes(int32_t rows, int64_t Np) {
 hipError_t launch_topk(int32_t rows, int64_t n_keys, int32_t window, int32_t budget, int32_t n_sink,
                        const float* scores, int32_t* idx, void* ws, hipStream_t st) {
     const int64_t Np = n_keys - window;
+    if (Np <= kRowMax) {
+        // short rows: one work-group per row, one launch (longer rows need
+        // the chunked kernels' parallelism)
+        hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, st,
+                           reinterpret_cast<const uint32_t*>(scores), idx, Np, window, budget, budget - window,
+                           n_sink);
+        return hipGetLastError();
+    }
     TopkGeom g;
     g.n_sink = n_sink;
     g.x = reinterpret_cast<const uint32_t*>(scores);
