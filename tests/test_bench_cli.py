@@ -51,3 +51,16 @@ def test_bench_line_carries_the_report_keys():
         assert key in roof, key
     cpu = line["cpu_baseline"]
     assert cpu["cores"] >= 1 and cpu["kind"] == "oracle" and isinstance(cpu["cpu_model"], str)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", ["--decode", "--csm", "--stats", "--lse-in"])
+def test_bench_other_modes_run(mode):
+    """Each of the other bench modes prints one JSON line with its roofline
+    (short runs, no CPU baseline)."""
+    import json
+
+    r = run(mode, "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["value"] > 0 and line["roofline"]["frac"] > 0
