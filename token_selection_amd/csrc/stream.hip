@@ -178,7 +178,12 @@ struct Smem {
 };
 
 // Stage the query rows of a segment's slab (row r -> head g*G + r/w, window
-// index r%w; rows past R are zero) and reset or load the per-row state.
+// index r%w; rows past R are zero) and reset or load the per-row state. The
+// rows pass through registers kStageLoads 16-byte loads per thread at a time,
+// which keeps this code (run once per segment) clear of the registers that
+// hold the next chunk's keys.
+constexpr int kStageLoads = 4;
+
 template <int D, int RBN, int PASS, bool ST>
 __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int tid) {
     constexpr int RP = RBN * 32;
@@ -194,19 +199,6 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
     const int rows = slab_rows(a, slab);
     const uint16_t* qbase = a.q + l * a.qs[0] + b * a.qs[1];
     __syncthreads();  // every wave is done with the previous segment's rows
-    uint4 qv[QPER];
-#pragma unroll
-    for (int u = 0; u < QPER; ++u) {
-        const int idx = tid + u * 256;
-        const int row = idx / CPK;
-        const int ch = idx - row * CPK;
-        qv[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (row < rows) {
-            const int h = h0 + row / a.w;
-            const int i = row % a.w;
-            qv[u] = *reinterpret_cast<const uint4*>(qbase + h * a.qs[2] + i * a.qs[3] + ch * 8);
-        }
-    }
     if (PASS == 1) {
         if constexpr (ST) {
             for (int i = tid; i < kWaves * RP; i += 256) (&sm.st[0][0])[i] = make_float4(kNegBig, 0.f, 0.f, 0.f);
@@ -217,17 +209,32 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int ti
         for (int row = tid; row < RP; row += 256) {
             const float l2 = row < rows ? a.lse2[(int64_t)slab * RP + row] : INFINITY;
             sm.lse[row] = l2;
-
         }
         if constexpr (ST)
             for (int i = tid; i < kWaves * RP; i += 256) (&sm.cnt[0][0])[i] = 0u;
     }
+#pragma unroll 1
+    for (int u0 = 0; u0 < QPER; u0 += kStageLoads) {
+        uint4 qv[kStageLoads];
 #pragma unroll
-    for (int u = 0; u < QPER; ++u) {
-        const int idx = tid + u * 256;
-        const int row = idx / CPK;
-        const int ch = idx - row * CPK;
-        if (row < RP) *reinterpret_cast<uint4*>(sm.q + row * QST + ch * 8) = qv[u];
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int idx = tid + (u0 + u) * 256;
+            const int row = idx / CPK;
+            const int ch = idx - row * CPK;
+            qv[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (u0 + u < QPER && row < rows) {
+                const int h = h0 + row / a.w;
+                const int i = row % a.w;
+                qv[u] = *reinterpret_cast<const uint4*>(qbase + h * a.qs[2] + i * a.qs[3] + ch * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int idx = tid + (u0 + u) * 256;
+            const int row = idx / CPK;
+            const int ch = idx - row * CPK;
+            if (u0 + u < QPER && row < RP) *reinterpret_cast<uint4*>(sm.q + row * QST + ch * 8) = qv[u];
+        }
     }
     __syncthreads();
 }
