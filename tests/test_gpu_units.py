@@ -32,6 +32,12 @@ def _topk_case(scores_np, n_keys, window, budget):
     # around the one-launch limit of 4096 prefix keys per row (one work-group per row up to it)
     (4096 + 8, 8, 1024, "rand"), (4096 + 9, 8, 1024, "rand"), (4096 + 8, 8, 4096 + 8, "ties"),
     (4096 + 8, 8, 3000, "ties"), (33, 1, 2, "const"), (2048, 32, 256, "zeros_and_ties"), (4096 + 8, 8, 9, "const"),
+    # rows of 32K keys (the chunked kernels)
+    (32768 + 8, 8, 2048, "rand"), (32768 + 9, 8, 2048, "rand"), (32768 + 8, 8, 32768 + 8, "ties"),
+    (32768 + 8, 8, 5000, "ties"), (32768 + 8, 8, 100, "const"), (32768 + 8, 8, 4000, "zeros_and_ties"),
+    # digit layouts: values over many octaves, within one ulp-scale band, of both signs
+    (20000, 8, 2048, "spread"), (20000, 8, 300, "narrow"), (20000, 16, 3000, "signed"), (3000, 8, 700, "narrow"),
+    (3000, 8, 500, "signed"), (4096 + 8, 8, 1500, "spread"),
 ])
 def test_topk_matches_oracle(n_keys, window, budget, kind):
     say("topk", n_keys, window, budget, kind)
@@ -43,10 +49,38 @@ def test_topk_matches_oracle(n_keys, window, budget, kind):
         s = rng.integers(0, 7, shape).astype(np.float32) * np.float32(0.125)
     elif kind == "const":
         s = np.full(shape, 0.3, dtype=np.float32)
+    elif kind == "spread":
+        s = np.exp2(rng.uniform(-120.0, 120.0, shape)).astype(np.float32)
+    elif kind == "narrow":
+        s = (np.float32(1.0) + rng.integers(0, 40, shape).astype(np.float32) * np.float32(2.0 ** -23))
+    elif kind == "signed":
+        s = rng.standard_normal(shape).astype(np.float32)
     else:
         s = rng.integers(0, 3, shape).astype(np.float32)
         s[..., ::5] = 0.0
     _topk_case(s, n_keys, window, budget)
+
+
+@pytest.mark.parametrize("n_keys,window,budget,n_sink", [
+    (3000, 8, 500, 4), (20000, 8, 2048, 16), (20000, 8, 40, 32), (20000, 8, 41, 32), (32768 + 8, 8, 4000, 1),
+    (70000, 64, 3000, 7),
+])
+def test_topk_sinks_match_oracle(n_keys, window, budget, n_sink):
+    """Protected sink positions through both kernel families (one work-group
+    per row up to 4096 keys, chunked above), including sinks filling every
+    slot and all slots but one."""
+    say("topk sinks", n_keys, window, budget, n_sink)
+    rng = np.random.default_rng(n_keys + n_sink)
+    s = rng.random((2, 3, n_keys - window)).astype(np.float32)
+    s[:, 1, :n_sink] = 0.0  # the sinks' own scores do not matter
+    t = torch.from_numpy(s).to(device())
+    idx = K.kvsel_topk(t, n_keys=n_keys, window=window, budget=budget, n_sink=n_sink)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(2):
+        for r in range(3):
+            exp = oracle.select_row(s[b, r].astype(np.float64), n_keys, window, budget, n_sink=n_sink)
+            assert np.array_equal(got[b, r], exp), (b, r, np.setxor1d(got[b, r], exp)[:10])
 
 
 def test_topk_negative_and_signed_zero():
