@@ -134,8 +134,14 @@ def main() -> int:
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch every kernel from Python each step instead of replaying HIP graphs")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
-                    help="write 1 GiB before every timed step (auto: when K is below 1 GiB, so that it cannot sit "
-                         "in the 256 MB memory-side cache from the previous step)")
+                    help="read 1 GiB before every timed step (auto: when the step's inputs are below 1 GiB, so "
+                         "that they cannot sit in the 256 MB memory-side cache from the previous step)")
+    ap.add_argument("--serial", dest="concurrent", action="store_false",
+                    help="run every call on one stream (default: the token-set head mean and top-k beside the "
+                         "per-head top-k, on a second stream)")
+    ap.add_argument("--check", action="store_true",
+                    help="after timing, compare every output of the timed step (graph replay or launches) with a "
+                         "serial eager step, bit for bit; exit 1 on a difference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -225,11 +231,37 @@ def main() -> int:
         else:
             K.kvsel_score_lse(q, k, lse_in, scores, window=w, pool_kernel=wl.pool_kernel, workspace=ws, desc=desc)
 
+    # The token-set chain (head mean, then its top-k: seven small launches)
+    # runs beside the per-head top-k on a second stream (same priority),
+    # joining back before the stage returns, so the stages stay in order;
+    # graph capture records the fork and join as dependencies. The gathers
+    # stay on one stream: each streams at full HBM rate, and a fork and join
+    # in the graph costs about 10 us (measured: gather stage 0.039 against
+    # 0.028 ms on the 32K workload).
+    aux = torch.cuda.Stream(dev)
+    mode = {"concurrent": args.concurrent}
+
+    def side_by_side(main_fn, side_fns):
+        if not mode["concurrent"] or not side_fns:
+            main_fn()
+            for f in side_fns:
+                f()
+            return
+        cur = torch.cuda.current_stream(dev)
+        aux.wait_stream(cur)
+        with torch.cuda.stream(aux):
+            for f in side_fns:
+                f()
+        main_fn()
+        cur.wait_stream(aux)
+
+    def tsp_chain():
+        K.kvsel_accumulate(scores, tsp["score"], mode=K.KVSEL_ACC_HEAD_MEAN)
+        K.kvsel_topk(tsp["score"], n_keys=N, window=w, budget=wl.tsp_budget, idx=tsp["idx"], workspace=tsp_ws)
+
     def stage_topk():
-        K.kvsel_topk(scores, n_keys=N, window=w, budget=wl.kv_budget, idx=idx, workspace=tk_ws)
-        if tsp is not None:
-            K.kvsel_accumulate(scores, tsp["score"], mode=K.KVSEL_ACC_HEAD_MEAN)
-            K.kvsel_topk(tsp["score"], n_keys=N, window=w, budget=wl.tsp_budget, idx=tsp["idx"], workspace=tsp_ws)
+        side_by_side(lambda: K.kvsel_topk(scores, n_keys=N, window=w, budget=wl.kv_budget, idx=idx, workspace=tk_ws),
+                     [tsp_chain] if tsp is not None else [])
 
     def stage_gather():
         K.kvsel_gather(k, idx, kc)
@@ -242,6 +274,14 @@ def main() -> int:
     def step():
         for fn in stages.values():
             fn()
+
+    def outputs():
+        out = {"scores": scores, "idx": idx, "kc": kc, "vc": vc}
+        if tsp is not None:
+            out.update({"tsp_" + n: t for n, t in tsp.items()})
+        if stats is not None:
+            out.update({"stats_" + n: t for n, t in stats.items()})
+        return out
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -263,12 +303,8 @@ def main() -> int:
         torch.cuda.synchronize()
     launch = {name: (graphs[name].replay if args.graph else fn) for name, fn in list(stages.items()) + [("step", step)]}
 
-    # cache hygiene: a workload whose K fits or nearly fits the 256 MB memory-
-    # side cache gets a 1 GiB write before every timed step (outside the
-    # timing), so that no step starts with K resident from the previous one
-    k_bytes = wl.compulsory_bytes()["k_read"]
-    flush = args.flush == "on" or (args.flush == "auto" and k_bytes < (1 << 30))
-    fbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+    flusher = cache_flusher(dev, wl.compulsory_bytes()["k_read"], args.flush)
+    flush = flusher is not None
 
     def mk():
         return torch.cuda.Event(enable_timing=True)
@@ -277,8 +313,8 @@ def main() -> int:
         """reps runs of fn, each between two events on the launch stream."""
         evs = [(mk(), mk()) for _ in range(reps)]
         for e0, e1 in evs:
-            if fbuf is not None:
-                fbuf.fill_(1)
+            if flusher is not None:
+                flusher()
             e0.record(stream)
             fn()
             e1.record(stream)
@@ -300,6 +336,18 @@ def main() -> int:
 
     ms_per_step = sum(step_ms) / len(step_ms)
     stage_ms = {n: med(x) for n, x in stage_runs.items()}
+
+    check = None
+    if args.check:
+        # the buffers now hold the last timed stage runs' results (score, top-k, gather in order); one
+        # serial eager step must reproduce every byte
+        got = {n: t.clone() for n, t in outputs().items()}
+        mode["concurrent"] = False
+        step()
+        torch.cuda.synchronize()
+        bad = [n for n, t in outputs().items()
+               if not torch.equal(t.contiguous().view(torch.uint8), got[n].contiguous().view(torch.uint8))]
+        check = "identical" if not bad else "differs: " + ", ".join(bad)
 
     cb = wl.compulsory_bytes()
     units = wl.units
@@ -339,6 +387,8 @@ def main() -> int:
                    "pool": wl.pool_kernel, "kv_budget": wl.kv_budget, "tsp_budget": wl.tsp_budget,
                    "lse": "computed (two passes)" if lse_in is None else "handed in (one pass)",
                    "pivot_stats": bool(args.stats), "launch": "hip graph" if args.graph else "eager",
+                   "token_set_chain": ("beside the per-head top-k" if args.concurrent else "after it")
+                   if wl.tsp_budget is not None else None,
                    "cache_flush_between_steps": bool(flush)},
         "hbm_gbs_whole_path": whole_gbs,
         "hbm_frac_whole_path": whole_gbs / HBM_PEAK_GBS,
@@ -358,13 +408,32 @@ def main() -> int:
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
     }
+    if check is not None:
+        line["check"] = check
     print(json.dumps(line))
-    return 0
+    return 0 if check in (None, "identical") else 1
 
 
-def timed(fn, stream, steps, warmup):
-    """Warm-up calls, then `steps` calls back to back, each between two HIP
-    events on the launch stream: (mean, median, min, max) ms per call."""
+def cache_flusher(dev, footprint_bytes: int, mode: str):
+    """Cache hygiene between timed calls: with mode "on", or "auto" and inputs
+    below 1 GiB (they could sit in the 256 MB memory-side cache from the
+    previous call), a function that reads a 1 GiB buffer; None otherwise. It
+    runs before a call's start event, outside the timing. A read, not a
+    write: a written buffer leaves that cache full of dirty lines, and the
+    timed call's first kernel would pay their write-back (on the batched
+    8 x 32K workload: pass 1 in 157 instead of 113 us)."""
+    import torch
+
+    if not (mode == "on" or (mode == "auto" and footprint_bytes < (1 << 30))):
+        return None
+    buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    return lambda: buf.sum()
+
+
+def timed(fn, stream, steps, warmup, flusher=None):
+    """Warm-up calls, then `steps` calls, each between two HIP events on the
+    launch stream (after `flusher`, if given): (mean, median, min, max) ms
+    per call."""
     import torch
 
     for _ in range(warmup):
@@ -372,6 +441,8 @@ def timed(fn, stream, steps, warmup):
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in evs:
+        if flusher is not None:
+            flusher()
         e0.record(stream)
         fn()
         e1.record(stream)
@@ -409,8 +480,9 @@ def bench_extra(args, K, get_workload, make_inputs) -> int:
         out = torch.empty((L * B, Hq, d), dtype=torch.float32, device=dev)
         ws = torch.empty(max(1, K.kvsel_decode_workspace_bytes(L * B, Hq, Hkv, d, bud)), dtype=torch.uint8,
                          device=dev)
+        flusher = cache_flusher(dev, kc.numel() * 2 + vc.numel() * 2, args.flush)
         ms, ms_med, ms_min, ms_max = timed(lambda: K.kvsel_decode_attention(qd, kc, vc, out=out, workspace=ws),
-                                           stream, args.steps, args.warmup)
+                                           stream, args.steps, args.warmup, flusher)
         units = L * B * Hkv * bud
         alg = 2 * units * d * 2 + L * B * Hq * d * (2 + 4)
         cpu = None
@@ -438,7 +510,8 @@ def bench_extra(args, K, get_workload, make_inputs) -> int:
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                 "data": "synthetic (seeded; no dataset or weights)",
                 "config": {"workload": "structkv_128k_16l compacted (4096 kept per KV head, 16 layers)",
-                           "decode_batch": L * B, "q_heads": Hq, "kv_heads": Hkv, "keys": bud, "head_dim": d},
+                           "decode_batch": L * B, "q_heads": Hq, "kv_heads": Hkv, "keys": bud, "head_dim": d,
+                           "cache_flush_between_steps": flusher is not None},
                 "roofline": {"bound": "hbm", "kernel": "kvsel_decode_attention (decode_kernel + combine)",
                              "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -455,8 +528,9 @@ def bench_extra(args, K, get_workload, make_inputs) -> int:
     S = wl.n_layers * wl.batch * wl.n_kv_heads
     n, d, chunk, ns, nr, rate = wl.n_keys, wl.head_dim, 64, 4, 32, 0.25
     nm = K.csm_merge_count(rate, n, ns, nr)
+    flusher = cache_flusher(dev, k.numel() * 2 + v.numel() * 2, args.flush)
     ms, ms_med, ms_min, ms_max = timed(lambda: K.kvsel_csm(k, v, chunk=chunk, n_sink=ns, n_recent=nr, n_merge=nm),
-                                       stream, args.steps, args.warmup)
+                                       stream, args.steps, args.warmup, flusher)
     n_out = n - nm
     alg = 2 * S * n * d * 2 + 2 * S * n_out * d * 2 + S * n_out * 4
     cpu = None
@@ -476,7 +550,8 @@ def bench_extra(args, K, get_workload, make_inputs) -> int:
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded; no dataset or weights)",
             "config": {"workload": "batched_8x32k_ar1 keys and values", "slabs": S, "tokens": n, "head_dim": d,
-                       "chunk": chunk, "n_sink": ns, "n_recent": nr, "rate": rate, "n_merge": nm},
+                       "chunk": chunk, "n_sink": ns, "n_recent": nr, "rate": rate, "n_merge": nm,
+                       "cache_flush_between_steps": flusher is not None},
             "roofline": {"bound": "hbm", "kernel": "kvsel_csm (match + select + merge)",
                          "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,

@@ -54,13 +54,34 @@ def test_bench_line_carries_the_report_keys():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("mode", ["--decode", "--csm", "--stats", "--lse-in"])
-def test_bench_other_modes_run(mode):
+@pytest.mark.parametrize("mode,flushed", [("--decode", True), ("--csm", False), ("--stats", False),
+                                          ("--lse-in", False)])
+def test_bench_other_modes_run(mode, flushed):
     """Each of the other bench modes prints one JSON line with its roofline
-    (short runs, no CPU baseline)."""
+    (short runs, no CPU baseline) and says whether a cache flush ran between
+    its timed calls: the decode cache (268 MB) is flushed, the CSM inputs
+    (1 GiB) and the 128K workload's K (4.3 GB) are not."""
     import json
 
     r = run(mode, "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
     assert r.returncode == 0, r.stderr[-2000:]
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["value"] > 0 and line["roofline"]["frac"] > 0
+    assert line["config"]["cache_flush_between_steps"] is flushed
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("workload,extra", [("llama8b_32k_tsp", ()), ("llama8b_32k_tsp", ("--no-graph",)),
+                                            ("batched_8x32k_ar1", ()), ("batched_8x32k_ar1", ("--stats",))])
+def test_bench_concurrent_step_matches_serial(workload, extra):
+    """The timed step (the token-set chain beside the per-head top-k on a
+    second stream where the workload has one), replayed from a HIP graph or
+    launched each step: every output must equal a serial eager step's, byte
+    for byte."""
+    import json
+
+    r = run("--workload", workload, *extra, "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--check")
+    assert r.returncode == 0, (r.stdout[-1000:], r.stderr[-2000:])
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["check"] == "identical"
+    assert line["config"]["token_set_chain"] == ("beside the per-head top-k" if workload.startswith("llama") else None)
