@@ -10,7 +10,8 @@
 //
 // The step reads every kept key and value once: it is HBM-bound, and the
 // group's G <= 8 query heads are too few rows for matrix cores to matter, so
-// the kernel is plain vector code. Each work-group takes one (b, g) and one
+// the kernel is vector code (the query-key products two bf16 pairs at a time
+// with v_dot2_f32_bf16, the rest in fp32). Each work-group takes one (b, g) and one
 // split of the keys; its 4 waves walk blocks of 16 keys (8 for G > 4). In a
 // block, lane (r, s) owns elements s*D/16 .. (s+1)*D/16 - 1 of rows r, r + 4, ..., for
 // the keys and for the values alike: 16 lanes read one row (coalesced), a
@@ -41,6 +42,8 @@ constexpr int rows_per_lane() {
     return G <= 2 ? 4 : G <= 4 ? (D == 128 ? 8 : 4) : 2;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 struct DecGeom {
     int32_t B, Hq, Hkv, G;
     int64_t n;
@@ -48,8 +51,6 @@ struct DecGeom {
     int64_t split_len;  // keys per split, a multiple of 64
     float c;            // scale * log2(e)
 };
-
-__device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // x moved across lanes by the DPP control CTRL (every lane valid).
 template <int CTRL>
@@ -146,12 +147,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
     const int kvh = bg - b * g.Hkv;
     const int r = lane >> 4;   // rows r, r + 4, ... of a block
     const int sl = lane & 15;  // elements sl*EL .. sl*EL + EL-1 of those rows
-    // this lane's slice of the group's queries, fp32
-    float qv[G][EL];
+    // this lane's slice of the group's queries, raw bf16 pairs (element 2i in the low half, as in a Slice)
+    uint32_t qw[G][EL / 2];
 #pragma unroll
     for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-        for (int e = 0; e < EL; ++e) qv[gg][e] = bf(q[((int64_t)b * g.Hq + kvh * G + gg) * D + sl * EL + e]);
+        for (int e2 = 0; e2 < EL / 2; ++e2)
+            qw[gg][e2] = *reinterpret_cast<const uint32_t*>(q + ((int64_t)b * g.Hq + kvh * G + gg) * D + sl * EL + 2 * e2);
     const int64_t key0 = (int64_t)split * g.split_len;
     const int64_t key1 = min(key0 + g.split_len, g.n);
     const uint16_t* kb = k + (int64_t)bg * g.n * D;
@@ -180,9 +182,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dec_wa
         for (int t = 0; t < kT; ++t) {
 #pragma unroll
             for (int gg = 0; gg < G; ++gg) {
+                // bf16 pairs multiplied and summed in fp32 by v_dot2_f32_bf16 (the products are exact)
                 float a = 0.f;
 #pragma unroll
-                for (int e = 0; e < EL; ++e) a += qv[gg][e] * elem<EL>(xk[t], e);
+                for (int e2 = 0; e2 < EL / 2; ++e2)
+                    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[gg][e2]),
+                                                        __builtin_bit_cast(bf16x2, xk[t].w[e2]), a, false);
                 s[t][gg] = a;
             }
         }
