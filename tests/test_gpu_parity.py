@@ -71,6 +71,60 @@ def test_ragged_shapes(case, path):
     check_all(wl, inp, gpu, ref)
 
 
+def layer_groups(L, B, Hq, Hkv, d, N, w):
+    """Layers per group of the streamed pass 2's layer sums for this shape
+    (average pool, one head group), or 0 where every layer keeps its own raw
+    row: as many layers per group as leave each of the 2 x n_CU work-group
+    slots a unit of 8192 keys of one (b, KV head)."""
+    n_wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    R = Hq // Hkv * w
+    rbn = 1
+    while rbn * 32 < R:
+        rbn *= 2
+    Np = N - w
+    if L < 2 or Np <= 0 or R > 256 or not ((d == 128 and rbn <= 4) or (d == 64 and rbn <= 8)):
+        return 0
+    per_group = B * Hkv * -(-Np // 8192)
+    n_groups = -(-n_wg // per_group)
+    return 0 if n_groups >= L else -(-L // n_groups)
+
+
+# (L, B, Hq, Hkv, d, N, w, pool, budget, KV heads checked, layers per group on 256 CUs)
+LAYER_SUM = [
+    (16, 1, 32, 8, 128, 5 * 8192 + 140, 32, 7, 2048, (0, 5), 2),  # 128 rows, 8 groups of 2 layers
+    (5, 4, 8, 8, 128, 3 * 8192 + 500, 16, 7, 1000, (3,), 2),      # groups of 2, 2 and 1 layers, 4 sequences
+    (3, 2, 128, 16, 64, 60000, 32, 5, 3000, (1, 14), 2),          # d = 64, 256 rows, groups of 2 and 1
+    (3, 4, 16, 16, 64, 4 * 8192 + 1008, 8, 7, 900, (7,), 2),      # 640 units on 512 work-groups
+]
+
+
+@pytest.mark.parametrize("case", LAYER_SUM, ids=lambda c: "-".join(map(str, c[:9])))
+def test_layer_sum_pass2(case):
+    """Calls whose pass 2 sums groups of layers in LDS (long prefixes, many
+    layers, average pool): every score and LSE of the checked KV heads against
+    the oracle's, the call added to earlier scores (accumulate), and the
+    single-pass call given the two-pass call's own LSE, which must reproduce
+    its scores up to that LSE's rounding."""
+    L, B, Hq, Hkv, d, N, w, pool, budget, hs, lg = case
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if n_cu == 256:  # the premise: this shape takes the layer-sum pass
+        assert layer_groups(L, B, Hq, Hkv, d, N, w) == lg
+    say("case layer sum", case, "layers per group", layer_groups(L, B, Hq, Hkv, d, N, w))
+    wl = TINY.with_(name="layer_sum", wid=500 + LAYER_SUM.index(case), dtype="bf16", n_layers=L, batch=B,
+                    n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool,
+                    kv_budget=budget, n_hubs=16)
+    inp = make_inputs(wl, threads=16, with_v=False)
+    ref = oracle_for(wl, inp, heads=hs)
+    gpu = run_gpu(wl, inp, with_gather=False)
+    check_all(wl, inp, gpu, ref, heads=hs)
+    prev = np.random.default_rng(5).uniform(0.0, 2.0, size=gpu["scores"].shape).astype(np.float32)
+    acc = run_gpu(wl, inp, accumulate_into=prev, with_gather=False, with_lse=False)
+    assert_scores_close(acc["scores"][:, list(hs)], prev[:, list(hs)] + ref["scores"][:, list(hs)])
+    one = run_gpu(wl, inp, lse_in=gpu["lse"], with_gather=False)
+    np.testing.assert_allclose(one["scores"].astype(np.float64), gpu["scores"].astype(np.float64), rtol=1e-5,
+                               atol=1e-30)
+
+
 def test_stream_path_refuses_other_shapes():
     """An explicit streaming choice on fp32 input is refused before any
     launch, with UNSUPPORTED, and nothing is written."""

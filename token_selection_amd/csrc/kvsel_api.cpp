@@ -209,6 +209,11 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         a.lse2 = reinterpret_cast<float*>(ws + p.stream.lse2_off);
         a.raw = reinterpret_cast<float*>(ws + p.stream.raw_off);
         a.l2tau = stats ? log2f(stats->small_p) : 0.f;
+        a.lg = 0;
+        a.n_lyr = g.L;
+        // pass 2 may sum the layers itself where pooling the sum equals summing the pooled layers
+        raw_layers = g.L * p.T;
+        if (!stats && desc->pool_type == KVSEL_POOL_AVG) raw_layers = kvsel::stream_layer_groups(p.stream, a, g.L);
         if (stats) {
             if (kvsel::launch_stream_stats(p.stream, a, lse_out, stats->entropy, stats->sum_p2, stats->n_below, hs) !=
                 hipSuccess)
@@ -222,7 +227,6 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
             return KVSEL_ERR_HIP;
         }
         raw = a.raw;
-        raw_layers = g.L * p.T;
         if (p.T > 1 && desc->pool_type == KVSEL_POOL_MAX && g.Np > 0) {
             // the max pool is not linear: add the head groups into the first
             // group's slices first, then pool layer by layer

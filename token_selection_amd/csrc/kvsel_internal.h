@@ -75,7 +75,11 @@ struct StreamArgs {
     int32_t spp;      // segments per slab (set per pass)
     int32_t seg_len;  // keys per segment, a multiple of the 256-key chunk
     int32_t n_range;  // keys the pass covers: N (pass 1, and pass 2 with statistics) or Np (pass 2)
-    int32_t n_seg;    // S * spp
+    int32_t n_seg;    // S * spp (layer-sum pass 2: units * lg)
+    // Layer-sum pass 2 (set by stream_layer_groups): the prefix keys' raw
+    // scores summed over groups of lg consecutive layers of the n_lyr, raw
+    // then [ceil(n_lyr / lg)][B*Hkv][Np]; lg = 0: one raw row per slab.
+    int32_t lg, n_lyr;
     float c, invG;
     float l2tau;   // statistics: log2 of the probability threshold of the count
     float2* part;  // [S][spp1][rp] per-segment (reference, sum) of every row, log2 domain
@@ -101,6 +105,10 @@ hipError_t launch_stream_stats(const StreamPlan& plan, StreamArgs a, float* lse_
                                int32_t* n_below, hipStream_t stream);
 // Pass 2 alone, on row LSEs already in a.lse2.
 hipError_t launch_stream_pass2(const StreamPlan& plan, StreamArgs a, hipStream_t stream);
+// Whether pass 2 sums the layers of an L-layer call itself (average pool
+// only: pooling is linear; one head group): sets a.lg (0: no) and a.n_lyr and
+// returns the number of raw rows per (b, KV head) the pool then sums.
+int stream_layer_groups(const StreamPlan& plan, StreamArgs& a, int L);
 
 hipError_t launch_accumulate(int32_t B, int32_t H, int64_t n, const float* src, float* dst, int mode,
                              hipStream_t stream);

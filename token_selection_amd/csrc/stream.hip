@@ -22,6 +22,12 @@
 // that, its query heads split into head groups, each a slab of its own over
 // the same keys (StreamArgs::T, Gs, S0).
 //
+// With LS (calls of several layers, average pool, one head group) pass 2 adds
+// up groups of layers itself: a work-group walks the layers of a group over
+// one key range, keeps each key's running sum in LDS and writes it once, so
+// raw holds one row per layer group instead of one per layer (pooling the sum
+// equals summing the pooled layers).
+//
 // No work-group waits for another: every slab is cut into segments of whole
 // 256-key chunks, work-group g takes segments g, g + grid, ..., and while it
 // computes one chunk the loads of its next chunk are in flight into a second
@@ -112,28 +118,76 @@ struct CountState {
     }
 };
 
+// Layer-sum pass 2 (LS): a unit is one key range of kLsKeys keys of one
+// (b, KV head) in a group of a.lg consecutive layers; its work-group walks the
+// group's layers over that range (the unit's slices) and keeps each key's sum
+// over them in LDS, one slot per lane and key (no other lane touches it), so
+// that raw holds one row per layer group instead of one per layer.
+constexpr int kLsChunks = 32;
+constexpr int kLsKeys = kLsChunks * kChunk;  // 8192 keys, 32 KB of LDS sums
+
 // Position in a work-group's sequence of chunks.
 struct Cursor {
-    int seg;    // segment index (slab * spp + part)
+    int seg;    // segment index: slab * spp + part, or with LS unit * lg + slice
     int first;  // first key of the chunk
     int end;    // end of the segment's key range
+    int slab;   // the segment's slab
+    int base;   // LS: the segment's first key
+    int out;    // LS: raw row of the unit (layer group * B*Hkv + b*Hkv + g)
+    int lsm;    // LS: bit 0 the group's first layer, bit 1 its last
 };
 
-__device__ __forceinline__ bool seg_range(const StreamArgs& a, int seg, int& first, int& end) {
-    const int part = seg % a.spp;
-    first = part * a.seg_len;
-    end = min(first + a.seg_len, a.n_range);
-    return first < end;
+template <bool LS>
+__device__ __forceinline__ bool seg_range(const StreamArgs& a, int seg, Cursor& c) {
+    int part;
+    c.seg = seg;
+    if constexpr (LS) {
+        // seg = unit * lg + slice, unit = (grp * B*Hkv + bg) * spp + part, layer = grp * lg + slice
+        const int unit = seg / a.lg, sl = seg - unit * a.lg;
+        const int gb = unit / a.spp;
+        part = unit - gb * a.spp;
+        const int BH = a.B * a.Hkv;
+        const int grp = gb / BH, bg = gb - grp * BH;
+        const int l = grp * a.lg + sl;
+        if (l >= a.n_lyr) return false;  // the last group holds fewer layers
+        c.slab = l * BH + bg;
+        c.out = gb;
+        c.lsm = (sl == 0 ? 1 : 0) | (sl == a.lg - 1 || l == a.n_lyr - 1 ? 2 : 0);
+    } else {
+        c.slab = seg / a.spp;
+        part = seg - c.slab * a.spp;
+        c.out = 0;
+        c.lsm = 0;
+    }
+    c.first = part * a.seg_len;
+    c.base = c.first;
+    c.end = min(c.first + a.seg_len, a.n_range);
+    return c.first < c.end;
 }
 
 // The chunk after c in this work-group's sequence; seg = -1 when there is none.
+template <bool LS>
 __device__ __forceinline__ Cursor advance(const StreamArgs& a, Cursor c) {
-    if (c.first + kChunk < c.end) return Cursor{c.seg, c.first + kChunk, c.end};
-    for (int seg = c.seg + (int)gridDim.x; seg < a.n_seg; seg += gridDim.x) {
-        int first, end;
-        if (seg_range(a, seg, first, end)) return Cursor{seg, first, end};
+    if (c.first + kChunk < c.end) {
+        c.first += kChunk;
+        return c;
     }
-    return Cursor{-1, 0, 0};
+    Cursor n;
+    if constexpr (LS) {
+        // the unit's next slice, else this work-group's next unit
+        int seg = c.seg + 1;
+        for (;;) {
+            if (seg % a.lg == 0) seg += ((int)gridDim.x - 1) * a.lg;
+            if (seg >= a.n_seg) break;
+            if (seg_range<true>(a, seg, n)) return n;
+            seg = (seg / a.lg + 1) * a.lg;  // past the last layer: the unit is done
+        }
+    } else {
+        for (int seg = c.seg + (int)gridDim.x; seg < a.n_seg; seg += gridDim.x)
+            if (seg_range<false>(a, seg, n)) return n;
+    }
+    n.seg = -1;
+    return n;
 }
 
 // Slabs are [T][S0]: head group t = slab / S0 of the (layer, b, KV head)
@@ -156,7 +210,7 @@ __device__ __forceinline__ int slab_rows(const StreamArgs& a, int slab) {
 template <int D>
 __device__ __forceinline__ void load_chunk(Frag<D>& f, const StreamArgs& a, const Cursor& c, int wave, int col,
                                            int hf) {
-    const uint16_t* kslab = slab_keys(a, c.seg / a.spp);
+    const uint16_t* kslab = slab_keys(a, c.slab);
     const int kbase = c.first + wave * kWaveKeys;
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
@@ -188,12 +242,11 @@ struct Smem {
 constexpr int kStageLoads = 4;
 
 template <int D, int RBN, int PASS, bool ST>
-__device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int seg, int tid) {
+__device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int slab, int tid) {
     constexpr int RP = RBN * 32;
     constexpr int QST = D + 8;
     constexpr int CPK = D / 8;  // 16-byte chunks per row
     constexpr int QPER = (RP * CPK + 255) / 256;
-    const int slab = seg / a.spp;
     const int s0 = slab % a.S0;
     const int g = s0 % a.Hkv;
     const int b = (s0 / a.Hkv) % a.B;
@@ -252,7 +305,7 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
     const int kbase = c.first + wave * kWaveKeys;
     if (kbase >= a.N) return;  // the chunk ends before this wave's keys
     const bool edge = kbase + kWaveKeys > a.Np;  // reaches the window (causal mask) or the end
-    const int rows = slab_rows(a, c.seg / a.spp);
+    const int rows = slab_rows(a, c.slab);
     const int rbn = (rows + 31) >> 5;  // row blocks holding this slab's rows
     if constexpr (!ST) {
         if (!edge) {
@@ -321,15 +374,17 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
     }
 }
 
-// Pass 2 on one chunk: raw score of each of this wave's prefix keys.
-template <int D, int RBN, bool ST>
-__device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamArgs& a, const Frag<D>& f,
-                                            const Cursor& c, int wave, int col, int hf, CountState<RBN>& cn) {
+// Pass 2 on one chunk: raw score of each of this wave's prefix keys (with LS
+// added to the key's sum over the layer group, stored at the group's last).
+template <int D, int RBN, bool ST, bool LS>
+__device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, float* lsum, const StreamArgs& a,
+                                            const Frag<D>& f, const Cursor& c, int wave, int col, int hf,
+                                            CountState<RBN>& cn) {
     constexpr int KS = D / 16;
     constexpr int QST = D + 8;
     const int kbase = c.first + wave * kWaveKeys;
     if (kbase >= a.n_range) return;  // no keys of this pass in this wave's range
-    const int slab = c.seg / a.spp;
+    const int slab = c.slab;
     const int rows = slab_rows(a, slab);
     const int rbn = (rows + 31) >> 5;  // row blocks holding this slab's rows
     float cs[kKB];
@@ -416,7 +471,17 @@ __device__ __forceinline__ void pass2_chunk(Smem<D, RBN, ST>& sm, const StreamAr
     const float v0 = cs[0] + __shfl_xor(cs[0], 32);
     const float v1 = cs[1] + __shfl_xor(cs[1], 32);
     const int j = kbase + hf * 32 + col;
-    if (j < a.Np) a.raw[(int64_t)slab * a.Np + j] = (hf ? v1 : v0) * a.invG;
+    const float val = (hf ? v1 : v0) * a.invG;
+    if constexpr (LS) {
+        float* p = lsum + (j - c.base);  // this lane's slot for key j
+        if (c.lsm & 2) {
+            if (j < a.Np) a.raw[(int64_t)c.out * a.Np + j] = ((c.lsm & 1) ? 0.f : *p) + val;
+        } else {
+            *p = (c.lsm & 1) ? val : *p + val;
+        }
+    } else if (j < a.Np) {
+        a.raw[(int64_t)slab * a.Np + j] = val;
+    }
 }
 
 // Pass 1, end of a segment: merge the waves' states and publish the partials.
@@ -495,18 +560,18 @@ __device__ __forceinline__ void pass2_finish(Smem<D, RBN, true>& sm, const Strea
 
 // One chunk with its keys in `f` while the next chunk's keys load into `g`.
 // Returns false once the work-group's sequence ends.
-template <int D, int RBN, int PASS, bool ST>
-__device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, const StreamArgs& a, Cursor& cur, Frag<D>& f,
-                                     Frag<D>& g, int tid, int wave, int col, int hf, RowState<RBN>& rs,
+template <int D, int RBN, int PASS, bool ST, bool LS>
+__device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, float* lsum, const StreamArgs& a, Cursor& cur,
+                                     Frag<D>& f, Frag<D>& g, int tid, int wave, int col, int hf, RowState<RBN>& rs,
                                      CountState<RBN>& cn) {
-    const Cursor nx = advance(a, cur);
+    const Cursor nx = advance<LS>(a, cur);
     // Issued on every step (the last one re-reads the current chunk): with a
     // fixed number of loads in flight the wait for `f` leaves `g`'s in flight.
     load_chunk<D>(g, a, nx.seg >= 0 ? nx : cur, wave, col, hf);
     if (PASS == 1)
         pass1_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf, rs);
     else
-        pass2_chunk<D, RBN, ST>(sm, a, f, cur, wave, col, hf, cn);
+        pass2_chunk<D, RBN, ST, LS>(sm, lsum, a, f, cur, wave, col, hf, cn);
     if (nx.seg != cur.seg) {
         if (PASS == 1) pass1_finish<D, RBN, ST>(sm, a, cur.seg, tid, rs);
         if constexpr (ST && PASS == 2) {
@@ -514,42 +579,47 @@ __device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, const StreamArgs& a, 
             pass2_finish<D, RBN>(sm, a, cur.seg, tid);
         }
         if (nx.seg < 0) return false;
-        stage<D, RBN, PASS, ST>(sm, a, nx.seg, tid);
+        stage<D, RBN, PASS, ST>(sm, a, nx.slab, tid);
     }
     cur = nx;
     return true;
 }
 
-template <int D, int RBN, int PASS, bool ST>
+// The kernel's LDS: the passes' own, and with LS the layer group's key sums.
+template <int D, int RBN, bool ST, bool LS>
+struct SmemK : Smem<D, RBN, ST> {
+    float lsum[LS ? kLsKeys : 1];
+};
+
+template <int D, int RBN, int PASS, bool ST, bool LS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 stream_kernel(StreamArgs a) {
-    __shared__ __attribute__((aligned(16))) Smem<D, RBN, ST> sm;
+    __shared__ __attribute__((aligned(16))) SmemK<D, RBN, ST, LS> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps chunk bounds scalar
     const int col = lane & 31;
     const int hf = lane >> 5;
 
-    Cursor cur{-1, 0, 0};
-    for (int seg = blockIdx.x; seg < a.n_seg; seg += gridDim.x) {
-        int first, end;
-        if (seg_range(a, seg, first, end)) {
-            cur = Cursor{seg, first, end};
-            break;
-        }
-    }
-    if (cur.seg < 0) return;
+    // the first segment of this work-group's first unit (LS: a unit's first
+    // slice always holds a layer) or its first segment with keys
+    const int lg = LS ? a.lg : 1;
+    Cursor cur;
+    bool found = false;
+    for (int seg = blockIdx.x * lg; seg < a.n_seg && !found; seg += gridDim.x * lg)
+        found = seg_range<LS>(a, seg, cur);
+    if (!found) return;
     Frag<D> fa, fb;
     RowState<RBN> rs;
     rs.reset();
     CountState<RBN> cn;
     cn.reset();
     load_chunk<D>(fa, a, cur, wave, col, hf);
-    stage<D, RBN, PASS, ST>(sm, a, cur.seg, tid);
+    stage<D, RBN, PASS, ST>(sm, a, cur.slab, tid);
 
     for (;;) {
-        if (!step<D, RBN, PASS, ST>(sm, a, cur, fa, fb, tid, wave, col, hf, rs, cn)) break;
-        if (!step<D, RBN, PASS, ST>(sm, a, cur, fb, fa, tid, wave, col, hf, rs, cn)) break;
+        if (!step<D, RBN, PASS, ST, LS>(sm, sm.lsum, a, cur, fa, fb, tid, wave, col, hf, rs, cn)) break;
+        if (!step<D, RBN, PASS, ST, LS>(sm, sm.lsum, a, cur, fb, fa, tid, wave, col, hf, rs, cn)) break;
     }
 }
 
@@ -678,13 +748,35 @@ typedef void (*stream_fn)(StreamArgs);
 template <int D, int PASS, bool ST>
 stream_fn pick_rbn(int RBN) {
     switch (RBN) {
-        case 1: return stream_kernel<D, 1, PASS, ST>;
-        case 2: return stream_kernel<D, 2, PASS, ST>;
-        case 4: return stream_kernel<D, 4, PASS, ST>;
-        case 8: return stream_kernel<D, 8, PASS, ST>;
+        case 1: return stream_kernel<D, 1, PASS, ST, false>;
+        case 2: return stream_kernel<D, 2, PASS, ST, false>;
+        case 4: return stream_kernel<D, 4, PASS, ST, false>;
+        case 8: return stream_kernel<D, 8, PASS, ST, false>;
         default: return nullptr;
     }
 }
+
+// Layer-sum pass 2: the instances whose LDS (query rows plus the 32 KB of key
+// sums) leaves room for two work-groups per compute unit.
+stream_fn pick_ls(int D, int RBN) {
+    if (D == 128) {
+        switch (RBN) {
+            case 1: return stream_kernel<128, 1, 2, false, true>;
+            case 2: return stream_kernel<128, 2, 2, false, true>;
+            case 4: return stream_kernel<128, 4, 2, false, true>;
+            default: return nullptr;
+        }
+    }
+    switch (RBN) {
+        case 1: return stream_kernel<64, 1, 2, false, true>;
+        case 2: return stream_kernel<64, 2, 2, false, true>;
+        case 4: return stream_kernel<64, 4, 2, false, true>;
+        case 8: return stream_kernel<64, 8, 2, false, true>;
+        default: return nullptr;
+    }
+}
+static_assert(sizeof(SmemK<128, 4, false, true>) <= 80 * 1024 && sizeof(SmemK<64, 8, false, true>) <= 80 * 1024,
+              "two layer-sum work-groups per compute unit");
 
 stream_fn pick(int D, int RBN, int PASS, bool ST = false) {
     if (ST) {
@@ -780,7 +872,32 @@ hipError_t launch_stream_stats(const StreamPlan& plan, StreamArgs a, float* lse_
     return hipGetLastError();
 }
 
+int stream_layer_groups(const StreamPlan& plan, StreamArgs& a, int L) {
+    a.lg = 0;
+    a.n_lyr = L;
+    if (L < 2 || a.T != 1 || a.Np <= 0 || !pick_ls(plan.head_dim, plan.rbn_cap)) return L * a.T;
+    // as many layers per group as leave every work-group slot of the grid a unit
+    const int64_t per_group = (int64_t)a.B * a.Hkv * ((a.Np + kLsKeys - 1) / kLsKeys);
+    const int64_t n_groups = (plan.n_wg + per_group - 1) / per_group;
+    if (n_groups >= L) return L;  // one layer per unit: the per-layer pass does the same work
+    a.lg = (int)((L + n_groups - 1) / n_groups);
+    return (L + a.lg - 1) / a.lg;
+}
+
 hipError_t launch_stream_pass2(const StreamPlan& plan, StreamArgs a, hipStream_t st) {
+    if (a.lg > 0 && a.Np > 0) {
+        // layer sums: units of kLsKeys keys of one (b, KV head) over a group of a.lg layers
+        stream_fn f2 = pick_ls(plan.head_dim, plan.rbn_cap);
+        if (!f2) return hipErrorInvalidValue;
+        a.seg_len = kLsKeys;
+        a.spp = (a.Np + kLsKeys - 1) / kLsKeys;
+        a.n_range = a.Np;
+        const int n_groups = (a.n_lyr + a.lg - 1) / a.lg;
+        const int units = n_groups * a.B * a.Hkv * a.spp;
+        a.n_seg = units * a.lg;
+        hipLaunchKernelGGL(f2, dim3((unsigned)(units < plan.n_wg ? units : plan.n_wg)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
     stream_fn f2 = pick(plan.head_dim, plan.rbn_cap, 2);
     if (!f2) return hipErrorInvalidValue;
     // pass 2 over the prefix keys
