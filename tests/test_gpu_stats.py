@@ -90,6 +90,7 @@ SHAPES = [
     (1, 2, 4, 2, 128, 40, 40, 7),       # w = N: no prefix, only window keys
     (1, 1, 4, 2, 128, 41, 40, 7),       # one prefix key
     (2, 1, 28, 4, 64, 2100, 64, 7),     # 448 rows: head groups of 4 and 3 heads, 2 layers
+    (5, 4, 8, 8, 128, 25076, 16, 7),    # 5 layers, 4 sequences, 8 KV heads, 25K keys
 ]
 
 
@@ -200,4 +201,10 @@ def test_full_size_sampled_heads(name):
         dn = np.abs(gpu["n_below"][l, b, h].astype(np.int64) - nb[0])
         if dn.any():
             assert (dn <= near_threshold(wl, inp, small_p, l, b, h)).all()
+    # the call's scores are kvsel_score's (checked against the oracle at full size elsewhere), up to
+    # the rounding of the two calls' LSE merges
+    q = to_dev(inp["q"], wl.dtype)
+    k = to_dev(inp["k"], wl.dtype)
+    plain = K.kvsel_score(q, k, window=wl.window, pool_kernel=wl.pool_kernel).cpu().numpy()
+    np.testing.assert_allclose(gpu["scores"].astype(np.float64), plain.astype(np.float64), rtol=1e-5, atol=1e-30)
     say(f"case stats {name}: done ({time.time() - t0:.1f}s)")
