@@ -115,8 +115,8 @@ def cpu_baseline(wl, inp, budget_s: float = 15.0, mode: str = "two-pass", lse=No
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="structkv_128k_16l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lse-in", action="store_true",
@@ -284,8 +284,7 @@ def main() -> int:
         return out
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        step()
+    step()  # the library's one-time set-up (device attributes, scratch lookups) happens outside any capture
     torch.cuda.synchronize()
     # one HIP graph per stage and one for the whole step (kernel nodes only:
     # the library launches no memset or copy)
@@ -305,6 +304,14 @@ def main() -> int:
 
     flusher = cache_flusher(dev, wl.compulsory_bytes()["k_read"], args.flush)
     flush = flusher is not None
+
+    # the warm-up steps, in the timed launch form and right before the timed
+    # region: the part lowers its clocks while idle (as during the graph
+    # capture above) and takes about ten steps of this load to raise them
+    for _ in range(args.warmup):
+        if flusher is not None:
+            flusher()
+        launch["step"]()
 
     def mk():
         return torch.cuda.Event(enable_timing=True)
