@@ -110,7 +110,7 @@ def test_layer_sum_pass2(case):
     if n_cu == 256:  # the premise: this shape takes the layer-sum pass
         assert layer_groups(L, B, Hq, Hkv, d, N, w) == lg
     say("case layer sum", case, "layers per group", layer_groups(L, B, Hq, Hkv, d, N, w))
-    wl = TINY.with_(name="layer_sum", wid=500 + LAYER_SUM.index(case), dtype="bf16", n_layers=L, batch=B,
+    wl = TINY.with_(name="layer_sum", wid=540 + LAYER_SUM.index(case), dtype="bf16", n_layers=L, batch=B,
                     n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_keys=N, window=w, pool_kernel=pool,
                     kv_budget=budget, n_hubs=16)
     inp = make_inputs(wl, threads=16, with_v=False)
