@@ -32,12 +32,15 @@ def _topk_case(scores_np, n_keys, window, budget):
     # around the one-launch limit of 4096 prefix keys per row (one work-group per row up to it)
     (4096 + 8, 8, 1024, "rand"), (4096 + 9, 8, 1024, "rand"), (4096 + 8, 8, 4096 + 8, "ties"),
     (4096 + 8, 8, 3000, "ties"), (33, 1, 2, "const"), (2048, 32, 256, "zeros_and_ties"), (4096 + 8, 8, 9, "const"),
-    # rows of 32K keys (the chunked kernels)
+    # rows of 32K keys
     (32768 + 8, 8, 2048, "rand"), (32768 + 9, 8, 2048, "rand"), (32768 + 8, 8, 32768 + 8, "ties"),
     (32768 + 8, 8, 5000, "ties"), (32768 + 8, 8, 100, "const"), (32768 + 8, 8, 4000, "zeros_and_ties"),
     # digit layouts: values over many octaves, within one ulp-scale band, of both signs
     (20000, 8, 2048, "spread"), (20000, 8, 300, "narrow"), (20000, 16, 3000, "signed"), (3000, 8, 700, "narrow"),
     (3000, 8, 500, "signed"), (4096 + 8, 8, 1500, "spread"),
+    # pooled-like rows (neighbouring positions share digits), and rows of 256K keys
+    (131072, 32, 4096, "smooth"), (32768 + 8, 8, 2048, "smooth"), (5000, 8, 600, "smooth"),
+    (262144 + 8, 8, 5000, "rand"), (262145 + 8, 8, 5000, "ties"), (262144 + 8, 8, 3000, "smooth"),
 ])
 def test_topk_matches_oracle(n_keys, window, budget, kind):
     say("topk", n_keys, window, budget, kind)
@@ -55,6 +58,10 @@ def test_topk_matches_oracle(n_keys, window, budget, kind):
         s = (np.float32(1.0) + rng.integers(0, 40, shape).astype(np.float32) * np.float32(2.0 ** -23))
     elif kind == "signed":
         s = rng.standard_normal(shape).astype(np.float32)
+    elif kind == "smooth":  # a 7-wide mean of heavy-tailed values, like pooled saliency
+        raw = np.exp(rng.standard_normal(shape[:-1] + (shape[-1] + 6,)) * 2.0)
+        c = np.cumsum(raw, axis=-1)
+        s = ((c[..., 6:] - np.concatenate([np.zeros(shape[:-1] + (1,)), c[..., :-7]], -1)) / 7).astype(np.float32)
     else:
         s = rng.integers(0, 3, shape).astype(np.float32)
         s[..., ::5] = 0.0
