@@ -211,6 +211,8 @@ kvsel_status_t score_impl(const kvsel_score_desc_t* desc, const void* q_win, con
         a.l2tau = stats ? log2f(stats->small_p) : 0.f;
         a.lg = 0;
         a.n_lyr = g.L;
+        a.spp1 = 0;
+        a.lse_out = nullptr;
         // pass 2 may sum the layers itself where pooling the sum equals summing the pooled layers
         raw_layers = g.L * p.T;
         if (!stats && desc->pool_type == KVSEL_POOL_AVG) raw_layers = kvsel::stream_layer_groups(p.stream, a, g.L);

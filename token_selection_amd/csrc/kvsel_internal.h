@@ -87,6 +87,11 @@ struct StreamArgs {
     uint32_t* cnt_part;  // statistics: [S][spp1][rp] per-segment counts of keys below the threshold
     float* lse2;   // [S][rp] row LSE2
     float* raw;    // [S][Np]
+    // Pass 2 of the two-pass call: > 0 when it merges pass 1's spp1 partials
+    // of a slab into the row LSEs itself (then writing lse_out [L][B][Hq][w]
+    // natural-log LSE, or nothing if null); 0: the row LSEs are read from lse2.
+    int32_t spp1;
+    float* lse_out;
 };
 
 struct StreamPlan {

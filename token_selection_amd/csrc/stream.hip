@@ -7,7 +7,8 @@
 //   stream_kernel<PASS=1>  per-row (reference, sum of exp2) partials of every
 //                          segment of a slab, causal mask applied;
 //   stream_merge_kernel    the partials of a slab's segments -> row LSE2 (and
-//                          the natural-log LSE the caller may ask for);
+//                          the natural-log LSE the caller may ask for), or
+//                          the same merge done by pass 2 as it stages a slab;
 //   stream_kernel<PASS=2>  per prefix key, sum over the rows of
 //                          exp2(c*x - LSE2), times 1/G -> raw scores.
 //
@@ -240,9 +241,18 @@ struct Smem {
 // which keeps this code (run once per segment) clear of the registers that
 // hold the next chunk's keys.
 constexpr int kStageLoads = 4;
+// Pass 2 merges the partials as it stages a slab while that costs each
+// thread at most this many of them (and without layer sums); otherwise a
+// merge launch runs first.
+constexpr int kStageMerge = 16;
 
+// Pass 2 of the two-pass call with a.spp1 > 0 also merges the slab's pass-1
+// partials into its row LSEs here (no merge launch): 256/RP threads per row,
+// each over every (256/RP)-th segment, their states merged across adjacent
+// lanes; the work-group staging key range 0 of the slab (`first`) also writes
+// the rows' natural-log LSE where the caller asked for it.
 template <int D, int RBN, int PASS, bool ST>
-__device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int slab, int tid) {
+__device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int slab, int tid, bool first) {
     constexpr int RP = RBN * 32;
     constexpr int QST = D + 8;
     constexpr int CPK = D / 8;  // 16-byte chunks per row
@@ -260,6 +270,30 @@ __device__ void stage(Smem<D, RBN, ST>& sm, const StreamArgs& a, int slab, int t
             for (int i = tid; i < kWaves * RP; i += 256) (&sm.st[0][0])[i] = make_float4(kNegBig, 0.f, 0.f, 0.f);
         } else {
             for (int i = tid; i < kWaves * RP; i += 256) (&sm.st[0][0])[i] = make_float2(kNegBig, 0.f);
+        }
+    } else if (!ST && a.spp1 > 0) {
+        constexpr int NSUB = 256 / RP;
+        const int row = tid / NSUB, sub = tid % NSUB;
+        float M = kNegBig, Z = 0.f;
+        if (row < rows) {
+            const float2* pp = a.part + (int64_t)slab * a.spp1 * RP + row;
+#pragma unroll 4
+            for (int p = sub; p < a.spp1; p += NSUB) {
+                const float2 v = pp[(int64_t)p * RP];
+                merge(M, Z, v.x, v.y);
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < NSUB; off <<= 1) {
+            const float om = __shfl_xor(M, off), oz = __shfl_xor(Z, off);
+            merge(M, Z, om, oz);
+        }
+        if (sub == 0) {
+            const float l2 = row < rows ? M + log2f(Z) : INFINITY;
+            sm.lse[row] = l2;
+            if (first && a.lse_out && row < rows)
+                a.lse_out[(((int64_t)l * a.B + b) * a.Hq + h0 + row / a.w) * a.w + row % a.w] =
+                    l2 * 0.69314718055994530942f;
         }
     } else {
         for (int row = tid; row < RP; row += 256) {
@@ -579,7 +613,7 @@ __device__ __forceinline__ bool step(Smem<D, RBN, ST>& sm, float* lsum, const St
             pass2_finish<D, RBN>(sm, a, cur.seg, tid);
         }
         if (nx.seg < 0) return false;
-        stage<D, RBN, PASS, ST>(sm, a, nx.slab, tid);
+        stage<D, RBN, PASS, ST>(sm, a, nx.slab, tid, nx.base == 0);
     }
     cur = nx;
     return true;
@@ -615,7 +649,7 @@ stream_kernel(StreamArgs a) {
     CountState<RBN> cn;
     cn.reset();
     load_chunk<D>(fa, a, cur, wave, col, hf);
-    stage<D, RBN, PASS, ST>(sm, a, cur.slab, tid);
+    stage<D, RBN, PASS, ST>(sm, a, cur.slab, tid, cur.base == 0);
 
     for (;;) {
         if (!step<D, RBN, PASS, ST, LS>(sm, sm.lsum, a, cur, fa, fb, tid, wave, col, hf, rs, cn)) break;
@@ -847,8 +881,16 @@ hipError_t launch_stream(const StreamPlan& plan, StreamArgs a, float* lse_out, h
     a.n_range = a.N;
     a.n_seg = a.S * plan.spp1;
     hipLaunchKernelGGL(f1, dim3((unsigned)(a.n_seg < plan.n_wg ? a.n_seg : plan.n_wg)), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(stream_merge_kernel, merge_grid(a), dim3(256), 0, st, a.part, plan.spp1, plan.rp,
-                       row_map(a), a.lse2, lse_out);
+    if ((int64_t)plan.spp1 * plan.rp <= 256 * kStageMerge && a.Np > 0 && a.lg == 0) {
+        // pass 2 merges each slab's partials itself as it stages the slab (not
+        // with layer sums: a work-group restages there every 32 chunks, and the
+        // merges then cost what the launch saves)
+        a.spp1 = plan.spp1;
+        a.lse_out = lse_out;
+    } else {
+        hipLaunchKernelGGL(stream_merge_kernel, merge_grid(a), dim3(256), 0, st, a.part, plan.spp1, plan.rp,
+                           row_map(a), a.lse2, lse_out);
+    }
     return launch_stream_pass2(plan, a, st);
 }
 
