@@ -324,10 +324,13 @@ __global__ __launch_bounds__(256) void raw_score_kernel(ScoreGeom g) {
 // Average pool (zero padded, divisor = kernel) of the raw scores summed over
 // the layers of the call, added to scores when accumulating. Pooling is
 // linear, so the layers are summed first and pooled once: each work-group
-// sums a 256-position tile plus a halo of r positions on each side, with
-// every layer's load issued before the first add, then pools from LDS.
-constexpr int kPoolTile = 256;
+// sums a tile of kPoolTile positions plus a halo of r positions on each side
+// into LDS, every thread its kPoolSlots positions (one per 256) with all of
+// their loads of a layer issued together, then pools from LDS. The layers add
+// in order, so the result does not depend on the tiling.
+constexpr int kPoolTile = 1024;
 constexpr int kPoolMaxR = 127;
+constexpr int kPoolSlots = (kPoolTile + 2 * kPoolMaxR + 255) / 256;  // 5
 __global__ __launch_bounds__(256) void pool_acc_kernel(const float* __restrict__ raw, float* __restrict__ scores,
                                                        int L, int64_t BH, int64_t Np, int kern, int accumulate) {
     __shared__ float tile[kPoolTile + 2 * kPoolMaxR];
@@ -335,45 +338,55 @@ __global__ __launch_bounds__(256) void pool_acc_kernel(const float* __restrict__
     const int64_t j0 = (int64_t)blockIdx.x * kPoolTile;
     const int r = (kern - 1) / 2;
     const int span = kPoolTile + 2 * r;
-    for (int t = threadIdx.x; t < span; t += 256) {
+    const float* p = raw + bh * Np;
+    const int64_t lstride = BH * Np;
+    bool in[kPoolSlots];
+    float sum[kPoolSlots];
+#pragma unroll
+    for (int u = 0; u < kPoolSlots; ++u) {
+        const int t = threadIdx.x + u * 256;
         const int64_t j = j0 - r + t;
-        float sum = 0.f;
-        if (j >= 0 && j < Np) {
-            const float* p = raw + bh * Np + j;
-            const int64_t lstride = BH * Np;
-            int l = 0;
-            for (; l + 8 <= L; l += 8) {
-                float v[8];
+        in[u] = t < span && j >= 0 && j < Np;
+        sum[u] = 0.f;
+    }
+#pragma unroll 4
+    for (int l = 0; l < L; ++l) {
+        const float* pl = p + (int64_t)l * lstride + j0 - r + threadIdx.x;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(l + u) * lstride];
+        for (int u = 0; u < kPoolSlots; ++u)
+            if (in[u]) sum[u] += pl[u * 256];
+    }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) sum += v[u];
-            }
-            for (; l < L; ++l) sum += p[(int64_t)l * lstride];
-        }
-        tile[t] = sum;
+    for (int u = 0; u < kPoolSlots; ++u) {
+        const int t = threadIdx.x + u * 256;
+        if (t < span) tile[t] = sum[u];
     }
     __syncthreads();
-    const int64_t j = j0 + threadIdx.x;
-    if (j >= Np) return;
-    float pooled = 0.f;
-    for (int t = 0; t < kern; ++t) pooled += tile[threadIdx.x + t];
-    const float val = pooled / (float)kern;
-    const int64_t o = bh * Np + j;
-    scores[o] = accumulate ? scores[o] + val : val;
+#pragma unroll
+    for (int u = 0; u < kPoolTile / 256; ++u) {
+        const int t0 = threadIdx.x + u * 256;
+        const int64_t j = j0 + t0;
+        if (j >= Np) break;
+        float pooled = 0.f;
+        for (int t = 0; t < kern; ++t) pooled += tile[t0 + t];
+        const float val = pooled / (float)kern;
+        const int64_t o = bh * Np + j;
+        scores[o] = accumulate ? scores[o] + val : val;
+    }
 }
 
 // Max pool variant: s[j] = max over t = -r..r of raw[j + t], positions outside
 // [0, Np) left out (scores are >= 0, so this equals zero padding). A max does
 // not commute with the sum over layers, so each layer is pooled on its own and
 // the pooled layers are added up.
+constexpr int kMaxPoolTile = 256;  // one position per thread
 __global__ __launch_bounds__(256) void pool_max_acc_kernel(const float* __restrict__ raw, float* __restrict__ scores,
                                                            int L, int64_t BH, int64_t Np, int kern, int accumulate) {
-    __shared__ float tile[kPoolTile + 2 * kPoolMaxR];
+    __shared__ float tile[kMaxPoolTile + 2 * kPoolMaxR];
     const int64_t bh = blockIdx.y;
-    const int64_t j0 = (int64_t)blockIdx.x * kPoolTile;
+    const int64_t j0 = (int64_t)blockIdx.x * kMaxPoolTile;
     const int r = (kern - 1) / 2;
-    const int span = kPoolTile + 2 * r;
+    const int span = kMaxPoolTile + 2 * r;
     const int64_t j = j0 + threadIdx.x;
     float acc = 0.f;
     for (int l = 0; l < L; ++l) {
@@ -500,12 +513,12 @@ hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64
                        int pool_type, int accumulate, hipStream_t st) {
     if (Np <= 0) return hipSuccess;
     if ((pool_kernel - 1) / 2 > kPoolMaxR || BH > 65535) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((Np + kPoolTile - 1) / kPoolTile), (unsigned)BH);
     if (pool_type == KVSEL_POOL_MAX)
-        hipLaunchKernelGGL(pool_max_acc_kernel, grid, dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel,
-                           accumulate);
+        hipLaunchKernelGGL(pool_max_acc_kernel, dim3((unsigned)((Np + kMaxPoolTile - 1) / kMaxPoolTile), (unsigned)BH),
+                           dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel, accumulate);
     else
-        hipLaunchKernelGGL(pool_acc_kernel, grid, dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel, accumulate);
+        hipLaunchKernelGGL(pool_acc_kernel, dim3((unsigned)((Np + kPoolTile - 1) / kPoolTile), (unsigned)BH), dim3(256),
+                           0, st, raw, scores, L, BH, Np, pool_kernel, accumulate);
     return hipGetLastError();
 }
 
