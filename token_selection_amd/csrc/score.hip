@@ -325,8 +325,8 @@ __global__ __launch_bounds__(256) void raw_score_kernel(ScoreGeom g) {
 // the layers of the call, added to scores when accumulating. Pooling is
 // linear, so the layers are summed first and pooled once: each work-group
 // sums a tile of kPoolTile positions plus a halo of r positions on each side
-// into LDS, every thread its kPoolSlots positions (one per 256) with all of
-// their loads of a layer issued together, then pools from LDS. The layers add
+// into LDS, every thread its kPoolSlots positions (one per 256) with their
+// loads of four layers issued together, then pools from LDS. The layers add
 // in order, so the result does not depend on the tiling.
 constexpr int kPoolTile = 1024;
 constexpr int kPoolMaxR = 127;
@@ -349,12 +349,21 @@ __global__ __launch_bounds__(256) void pool_acc_kernel(const float* __restrict__
         in[u] = t < span && j >= 0 && j < Np;
         sum[u] = 0.f;
     }
-#pragma unroll 4
-    for (int l = 0; l < L; ++l) {
-        const float* pl = p + (int64_t)l * lstride + j0 - r + threadIdx.x;
+    // four layers' loads (20 per thread) in flight before their adds, which
+    // keep the layers' order
+    for (int l = 0; l < L; l += 4) {
+        float v[4][kPoolSlots];
 #pragma unroll
-        for (int u = 0; u < kPoolSlots; ++u)
-            if (in[u]) sum[u] += pl[u * 256];
+        for (int q = 0; q < 4; ++q) {
+            const bool lq = l + q < L;
+            const float* pl = p + (int64_t)(l + q) * lstride + j0 - r + threadIdx.x;
+#pragma unroll
+            for (int u = 0; u < kPoolSlots; ++u) v[q][u] = (lq && in[u]) ? pl[u * 256] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < kPoolSlots; ++u) sum[u] += v[q][u];
     }
 #pragma unroll
     for (int u = 0; u < kPoolSlots; ++u) {
