@@ -79,7 +79,8 @@ def _cores() -> int:
     return max(1, min(16, n))
 
 
-def cpu_baseline(wl, inp, budget_s: float = 15.0, mode: str = "two-pass", lse=None, small_p=None) -> dict:
+def cpu_baseline(wl, inp, budget_s: float = 15.0, mode: str = "two-pass", lse=None, small_p=None,
+                 pool_type: str = "avg") -> dict:
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: the first n layers of every sequence and KV head through
     score -> accumulate -> select -> gather (with the LSE handed in, or plus
@@ -93,7 +94,7 @@ def cpu_baseline(wl, inp, budget_s: float = 15.0, mode: str = "two-pass", lse=No
         t0 = time.perf_counter()
         oracle.pipeline(inp["q"][:n], inp["k"][:n], inp["v"][:n], dtype=wl.dtype, window=wl.window,
                         pool_kernel=wl.pool_kernel, kv_budget=wl.kv_budget, threads=cores,
-                        lse_in=None if lse is None else lse[:n])
+                        lse_in=None if lse is None else lse[:n], pool_type=pool_type)
         if mode == "stats":
             oracle.row_stats_all(inp["q"][:n], inp["k"][:n], wl.dtype, small_p, threads=cores)
         return time.perf_counter() - t0
@@ -108,7 +109,8 @@ def cpu_baseline(wl, inp, budget_s: float = 15.0, mode: str = "two-pass", lse=No
     units = n * wl.batch * wl.n_kv_heads * wl.n_keys
     return {"value": units / t, "unit": "keys/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {wl.n_layers} layers x {wl.batch} seq x {wl.n_kv_heads} KV heads x {wl.n_keys} keys "
-                      f"(score{' from the given LSE' if lse is not None else ''}, layer sum, select, K/V gather"
+                      f"(score{' from the given LSE' if lse is not None else ''}{', max pool' if pool_type == 'max' else ''}, "
+                      f"layer sum, select, K/V gather"
                       f"{', row statistics' if mode == 'stats' else ''}) in {t:.1f} s on {cores} threads"}
 
 
@@ -125,6 +127,9 @@ def main() -> int:
     ap.add_argument("--stats", action="store_true",
                     help="score with the pivot statistics of every window row (kvsel_score_stats, then "
                          "kvsel_layer_summary), as StructKV's pivot detection runs it")
+    ap.add_argument("--max-pool", action="store_true",
+                    help="pool each layer's raw scores with the max pool (then sum the layers) instead of the "
+                         "average pool")
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step of attention over the 16-layer 128K workload's compacted cache "
                          "(kvsel_decode_attention) instead of the selection path")
@@ -189,7 +194,8 @@ def main() -> int:
     B, Hkv, N, w = wl.batch, wl.n_kv_heads, wl.n_keys, wl.window
     scores = torch.empty((B, Hkv, N - w), dtype=torch.float32, device=dev)
     idx = torch.empty((B, Hkv, wl.kv_budget), dtype=torch.int32, device=dev)
-    desc = K.score_desc(q, k, w, wl.pool_kernel)
+    pool_type = K.KVSEL_POOL_MAX if args.max_pool else K.KVSEL_POOL_AVG
+    desc = K.score_desc(q, k, w, wl.pool_kernel, 0.0, pool_type)
     ws = torch.empty(max(1, K.kvsel_score_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     kc = torch.empty((wl.n_layers, B, Hkv, wl.kv_budget, wl.head_dim), dtype=k.dtype, device=dev)
     vc = torch.empty_like(kc)
@@ -363,6 +369,8 @@ def main() -> int:
     achieved = score_alg_bytes / (stage_ms["score"] / 1e3) / 1e9
     whole_gbs = cb["total"] / (ms_per_step / 1e3) / 1e9
     kernel_name = ("kvsel_score_stats" if args.stats else "kvsel_score" if lse_in is None else "kvsel_score_lse")
+    if args.max_pool:
+        kernel_name += "_maxpool"  # its own profile: the max pool reads every layer's raw scores
     traffic = recorded_traffic(kernel_name, STATS_SOURCES if args.stats else SCORE_SOURCES, wl.name)
 
     cpu = None
@@ -370,7 +378,7 @@ def main() -> int:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, inp, mode="stats" if args.stats else "lse-in" if lse_in is not None else "two-pass",
                            lse=None if lse_in is None else lse_in.cpu().numpy().astype(np.float64),
-                           small_p=small_p)
+                           small_p=small_p, pool_type="max" if args.max_pool else "avg")
         cpu["cpu_model"] = cpu_model()
 
     line = {
@@ -391,7 +399,8 @@ def main() -> int:
         "data": "synthetic (seeded; no dataset or weights)",
         "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "q_heads": wl.n_q_heads,
                    "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "n_keys": wl.n_keys, "window": wl.window,
-                   "pool": wl.pool_kernel, "kv_budget": wl.kv_budget, "tsp_budget": wl.tsp_budget,
+                   "pool": wl.pool_kernel, "pool_type": "max" if args.max_pool else "avg",
+                   "kv_budget": wl.kv_budget, "tsp_budget": wl.tsp_budget,
                    "lse": "computed (two passes)" if lse_in is None else "handed in (one pass)",
                    "pivot_stats": bool(args.stats), "launch": "hip graph" if args.graph else "eager",
                    "token_set_chain": ("beside the per-head top-k" if args.concurrent else "after it")
@@ -407,7 +416,8 @@ def main() -> int:
                      "kernel": ("kvsel_score_stats (stream_kernel pass 1 + merge + pass 2 + count + pool + "
                                 "layer summary)" if args.stats else
                                 "kvsel_score (stream_kernel pass 1 + merge + pass 2 + pool)" if lse_in is None
-                                else "kvsel_score_lse (stream_kernel pass 2 + pool)"),
+                                else "kvsel_score_lse (stream_kernel pass 2 + pool)")
+                     + (", max pool" if args.max_pool else ""),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "traffic_gbs": None if traffic is None else traffic / (stage_ms["score"] / 1e3) / 1e9,

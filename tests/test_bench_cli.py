@@ -55,7 +55,7 @@ def test_bench_line_carries_the_report_keys():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("mode,flushed", [("--decode", True), ("--csm", False), ("--stats", False),
-                                          ("--lse-in", False)])
+                                          ("--lse-in", False), ("--max-pool", False)])
 def test_bench_other_modes_run(mode, flushed):
     """Each of the other bench modes prints one JSON line with its roofline
     (short runs, no CPU baseline) and says whether a cache flush ran between
@@ -68,11 +68,14 @@ def test_bench_other_modes_run(mode, flushed):
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["value"] > 0 and line["roofline"]["frac"] > 0
     assert line["config"]["cache_flush_between_steps"] is flushed
+    if mode == "--max-pool":
+        assert line["config"]["pool_type"] == "max"
 
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("workload,extra", [("llama8b_32k_tsp", ()), ("llama8b_32k_tsp", ("--no-graph",)),
-                                            ("batched_8x32k_ar1", ()), ("batched_8x32k_ar1", ("--stats",))])
+                                            ("batched_8x32k_ar1", ()), ("batched_8x32k_ar1", ("--stats",)),
+                                            ("batched_8x32k_ar1", ("--max-pool",))])
 def test_bench_concurrent_step_matches_serial(workload, extra):
     """The timed step (the token-set chain beside the per-head top-k on a
     second stream where the workload has one), replayed from a HIP graph or

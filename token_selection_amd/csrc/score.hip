@@ -387,32 +387,63 @@ __global__ __launch_bounds__(256) void pool_acc_kernel(const float* __restrict__
 // Max pool variant: s[j] = max over t = -r..r of raw[j + t], positions outside
 // [0, Np) left out (scores are >= 0, so this equals zero padding). A max does
 // not commute with the sum over layers, so each layer is pooled on its own and
-// the pooled layers are added up.
-constexpr int kMaxPoolTile = 256;  // one position per thread
+// the pooled layers are added up (in layer order). Tiles as in the average
+// pool: each thread loads its kPoolSlots positions of four layers into
+// registers together, then per layer they pass through LDS for the window max.
 __global__ __launch_bounds__(256) void pool_max_acc_kernel(const float* __restrict__ raw, float* __restrict__ scores,
                                                            int L, int64_t BH, int64_t Np, int kern, int accumulate) {
-    __shared__ float tile[kMaxPoolTile + 2 * kPoolMaxR];
+    __shared__ float tile[kPoolTile + 2 * kPoolMaxR];
     const int64_t bh = blockIdx.y;
-    const int64_t j0 = (int64_t)blockIdx.x * kMaxPoolTile;
+    const int64_t j0 = (int64_t)blockIdx.x * kPoolTile;
     const int r = (kern - 1) / 2;
-    const int span = kMaxPoolTile + 2 * r;
-    const int64_t j = j0 + threadIdx.x;
-    float acc = 0.f;
-    for (int l = 0; l < L; ++l) {
-        const float* p = raw + ((int64_t)l * BH + bh) * Np;
-        __syncthreads();  // the previous layer's tile has been read
-        for (int t = threadIdx.x; t < span; t += 256) {
-            const int64_t jj = j0 - r + t;
-            tile[t] = (jj >= 0 && jj < Np) ? p[jj] : -INFINITY;
-        }
-        __syncthreads();
-        float m = -INFINITY;
-        for (int t = 0; t < kern; ++t) m = fmaxf(m, tile[threadIdx.x + t]);
-        acc += m;
+    const int span = kPoolTile + 2 * r;
+    const float* p = raw + bh * Np;
+    const int64_t lstride = BH * Np;
+    bool in[kPoolSlots];
+#pragma unroll
+    for (int u = 0; u < kPoolSlots; ++u) {
+        const int t = threadIdx.x + u * 256;
+        const int64_t j = j0 - r + t;
+        in[u] = t < span && j >= 0 && j < Np;
     }
-    if (j >= Np) return;
-    const int64_t o = bh * Np + j;
-    scores[o] = accumulate ? scores[o] + acc : acc;
+    float acc[kPoolTile / 256];
+#pragma unroll
+    for (int k = 0; k < kPoolTile / 256; ++k) acc[k] = 0.f;
+    for (int l = 0; l < L; l += 4) {
+        float v[4][kPoolSlots];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool lq = l + q < L;
+            const float* pl = p + (int64_t)(l + q) * lstride + j0 - r + threadIdx.x;
+#pragma unroll
+            for (int u = 0; u < kPoolSlots; ++u) v[q][u] = (lq && in[u]) ? pl[u * 256] : -INFINITY;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (l + q >= L) break;
+            __syncthreads();  // the previous layer's tile has been read
+#pragma unroll
+            for (int u = 0; u < kPoolSlots; ++u) {
+                const int t = threadIdx.x + u * 256;
+                if (t < span) tile[t] = v[q][u];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < kPoolTile / 256; ++k) {
+                const int t0 = threadIdx.x + k * 256;
+                float m = -INFINITY;
+                for (int t = 0; t < kern; ++t) m = fmaxf(m, tile[t0 + t]);
+                acc[k] += m;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPoolTile / 256; ++k) {
+        const int64_t j = j0 + threadIdx.x + k * 256;
+        if (j >= Np) break;
+        const int64_t o = bh * Np + j;
+        scores[o] = accumulate ? scores[o] + acc[k] : acc[k];
+    }
 }
 
 // Row LSE2 of every slab from a handed-in natural-log LSE (prefill attention
@@ -522,12 +553,12 @@ hipError_t launch_pool(const float* raw, float* scores, int L, int64_t BH, int64
                        int pool_type, int accumulate, hipStream_t st) {
     if (Np <= 0) return hipSuccess;
     if ((pool_kernel - 1) / 2 > kPoolMaxR || BH > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((Np + kPoolTile - 1) / kPoolTile), (unsigned)BH);
     if (pool_type == KVSEL_POOL_MAX)
-        hipLaunchKernelGGL(pool_max_acc_kernel, dim3((unsigned)((Np + kMaxPoolTile - 1) / kMaxPoolTile), (unsigned)BH),
-                           dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel, accumulate);
+        hipLaunchKernelGGL(pool_max_acc_kernel, grid, dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel,
+                           accumulate);
     else
-        hipLaunchKernelGGL(pool_acc_kernel, dim3((unsigned)((Np + kPoolTile - 1) / kPoolTile), (unsigned)BH), dim3(256),
-                           0, st, raw, scores, L, BH, Np, pool_kernel, accumulate);
+        hipLaunchKernelGGL(pool_acc_kernel, grid, dim3(256), 0, st, raw, scores, L, BH, Np, pool_kernel, accumulate);
     return hipGetLastError();
 }
 
