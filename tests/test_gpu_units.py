@@ -98,7 +98,10 @@ def test_topk_negative_and_signed_zero():
     _topk_case(s, 12, 2, 7)
 
 
-@pytest.mark.parametrize("row_bytes,idx_heads", [(256, 4), (256, 1), (128, 4), (8192, 1), (6, 4), (100, 1)])
+# Row sizes of both 16-byte kernel forms: slab form with 4 units per item
+# (64, 128, 256, 8192 bytes) or 1 (16, 32), general form (48, 192); byte copy (6, 100).
+@pytest.mark.parametrize("row_bytes,idx_heads", [(256, 4), (256, 1), (128, 4), (8192, 1), (16, 4), (32, 1),
+                                                 (64, 1), (48, 4), (192, 4), (6, 4), (100, 1)])
 def test_gather_bit_exact(row_bytes, idx_heads):
     say("gather", row_bytes, idx_heads)
     rng = np.random.default_rng(row_bytes)
@@ -113,6 +116,20 @@ def test_gather_bit_exact(row_bytes, idx_heads):
         for b in range(B):
             exp = oracle.gather_rows(src[l, b], idx[b].astype(np.int64))
             assert exp.tobytes() == got[l, b].tobytes()
+
+
+def test_gather_grid_stride():
+    """More work items per slab than one grid row holds (8200 rows of 8 KB:
+    1 049 600 items against 4096 work-groups of 256), so items loop."""
+    say("gather grid stride")
+    rng = np.random.default_rng(21)
+    N, budget, row_bytes = 9000, 8200, 8192
+    src = rng.integers(0, 256, (1, 1, 2, N, row_bytes), dtype=np.uint8)
+    idx = np.stack([np.sort(rng.choice(N, budget, replace=False)) for _ in range(2)])[None].astype(np.int32)
+    out = K.kvsel_gather(torch.from_numpy(src).to(device()), torch.from_numpy(idx).to(device()))
+    torch.cuda.synchronize()
+    exp = oracle.gather_rows(src[0, 0], idx[0].astype(np.int64))
+    assert exp.tobytes() == out.cpu().numpy()[0, 0].tobytes()
 
 
 def test_gather_strided_source_and_bad_indices():

@@ -51,6 +51,53 @@ __global__ __launch_bounds__(256) void gather16_kernel(GatherGeom g, uint4* __re
     }
 }
 
+// Slab form of the 16-byte gather, for rows whose unit count is a power of
+// two times U: grid row y is one (layer, b, head) slab, so the source base and
+// index row are set once per work-group, and each work item is one
+// (kept row, lane slot) pair copying U units, slot q taking units q, q + ipr, ...
+// (ipr = units per row / U). A row's ipr lanes thus read and write contiguous
+// 16*ipr-byte pieces per load, and no work item divides by a run-time size.
+struct GatherSlab {
+    const char* src;
+    int64_t s0, s1, s2, s3;  // byte strides over (layer, b, head, row)
+    const int32_t* idx;
+    int32_t B, H, idx_heads, budget;
+    int64_t n_src;
+    int32_t cpr;        // units per row
+    int32_t ipr_shift;  // log2(units per row / U)
+    int32_t items;      // budget << ipr_shift
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int U>
+__global__ __launch_bounds__(256) void gather16_slab_kernel(GatherSlab g, uint4* __restrict__ dst) {
+    const int slab = blockIdx.y;  // (l*B + b)*H + h
+    const int h = slab % g.H;
+    const int lb = slab / g.H;
+    const int b = lb % g.B;
+    const int l = lb / g.B;
+    const int32_t* idx = g.idx + (int64_t)(b * g.idx_heads + (g.idx_heads == 1 ? 0 : h)) * g.budget;
+    const char* src = g.src + l * g.s0 + b * g.s1 + h * g.s2;
+    uint4* out = dst + (int64_t)slab * g.budget * g.cpr;
+    const int ipr = 1 << g.ipr_shift;
+    for (int it = blockIdx.x * 256 + threadIdx.x; it < g.items; it += gridDim.x * 256) {
+        const int t = it >> g.ipr_shift;
+        const int q = it & (ipr - 1);
+        const int32_t j = idx[t];
+        const bool valid = j >= 0 && (int64_t)j < g.n_src;
+        const uint4* s = reinterpret_cast<const uint4*>(src + (valid ? (int64_t)j : 0) * g.s3) + q;
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = valid ? s[u * ipr] : make_uint4(0u, 0u, 0u, 0u);
+        // non-temporal stores: the output is not read again soon; kept out of
+        // the caches, it no longer delays the reads of the copy that follows
+        u32x4* o = reinterpret_cast<u32x4*>(out + (int64_t)t * g.cpr + q);
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v[u]), o + u * ipr);
+    }
+}
+
 __global__ __launch_bounds__(256) void gather1_kernel(GatherGeom g, char* __restrict__ dst) {
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < g.total;
          c += (int64_t)gridDim.x * blockDim.x) {
@@ -109,6 +156,38 @@ hipError_t launch_gather(int32_t L, int32_t B, int32_t H, int32_t idx_heads, int
     bool vec = (row_bytes % 16 == 0) && (((uintptr_t)src | (uintptr_t)dst) % 16 == 0);
     for (int i = 0; i < 4; ++i) vec = vec && (s[i] % 16 == 0);
     if (vec) {
+        // the slab form: whole powers of two of 4 units (64 bytes) per row, or
+        // rows of 1 or 2 units, with the grid rows and work items in range
+        const int64_t cpr = row_bytes / 16;
+        const int u = cpr % 4 == 0 ? 4 : 1;
+        const int64_t ipr = cpr / u;
+        const int64_t slabs = (int64_t)L * B * H;
+        if ((ipr & (ipr - 1)) == 0 && slabs <= 65535 && (int64_t)budget * ipr < ((int64_t)1 << 31)) {
+            GatherSlab gs;
+            gs.src = g.src;
+            gs.s0 = s[0];
+            gs.s1 = s[1];
+            gs.s2 = s[2];
+            gs.s3 = s[3];
+            gs.idx = idx;
+            gs.B = B;
+            gs.H = H;
+            gs.idx_heads = idx_heads;
+            gs.budget = budget;
+            gs.n_src = n_src_rows;
+            gs.cpr = (int32_t)cpr;
+            gs.ipr_shift = 0;
+            while (((int64_t)1 << gs.ipr_shift) < ipr) ++gs.ipr_shift;
+            gs.items = (int32_t)((int64_t)budget * ipr);
+            int64_t bx = ((int64_t)gs.items + 255) / 256;
+            if (bx > 4096) bx = 4096;
+            const dim3 grid((unsigned)bx, (unsigned)slabs);
+            if (u == 4)
+                hipLaunchKernelGGL(gather16_slab_kernel<4>, grid, dim3(256), 0, st, gs, static_cast<uint4*>(dst));
+            else
+                hipLaunchKernelGGL(gather16_slab_kernel<1>, grid, dim3(256), 0, st, gs, static_cast<uint4*>(dst));
+            return hipGetLastError();
+        }
         g.cpr = row_bytes / 16;
         g.total = rows * g.cpr;
         hipLaunchKernelGGL(gather16_kernel, dim3(grid_for(g.total)), dim3(256), 0, st, g, static_cast<uint4*>(dst));
