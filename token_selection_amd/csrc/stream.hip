@@ -352,11 +352,17 @@ __device__ __forceinline__ void pass1_chunk(Smem<D, RBN, ST>& sm, const StreamAr
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     qf[ks] = *reinterpret_cast<const bf16x8*>(sm.q + (rb * 32 + col) * QST + ks * 16 + hf * 8);
-                // lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf)
+                // lane holds row rb*32 + col and keys kbase + kb*32 + tile_row(v, hf);
+                // summed on the running reference, the block just adds to the running sum
                 float m;
-                float z = pass1_fast<D, kKB>(f.v, qf, a.c, m);
-                if (__any(!(z < kOverflow))) z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
-                merge(rs.m[rb], rs.z[rb], m, z);
+                float z = pass1_fast<D, kKB>(f.v, qf, a.c, rs.m[rb], m);
+                if (__any(!(z < kOverflow))) {
+                    z = pass1_max<D, kKB, false>(f.v, qf, a.c, kbase, hf, 0, m);
+                    merge(rs.m[rb], rs.z[rb], m, z);
+                } else {
+                    rs.z[rb] = rs.m[rb] > kNegBig ? rs.z[rb] + z : z;
+                    rs.m[rb] = m;
+                }
             }
             return;
         }

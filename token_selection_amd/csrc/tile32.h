@@ -60,17 +60,20 @@ __device__ __forceinline__ f32x16 logits(const bf16x8 (&a)[KS], const bf16x8 (&b
     return acc;
 }
 
-// Pass 1, common case: the lane's first logit is the reference. Any logit of
-// the row is a valid reference as far as the final LSE goes (partials are
-// merged by rescaling to a common one); it only has to keep exp2 in range, and
-// a sum of kOverflow or more (or inf) sends the block to pass1_max. The
-// exponentials of block kb run while block kb+1 is in the matrix core.
+// Pass 1, common case: the reference is the lane's running one (`run`), or
+// its first logit while it has none (run == kNegBig). Any value is a valid
+// reference as far as the final LSE goes (partials are merged by rescaling to
+// a common one); it only has to keep exp2 in range, and a sum of kOverflow or
+// more (or inf) sends the block to pass1_max. Keys far below the reference
+// add exp2 terms that underflow to zero next to a sum of at least 1 (the
+// reference logit's own term, or the row maximum's). The exponentials of
+// block kb run while block kb+1 is in the matrix core.
 template <int D, int KB>
 __device__ __forceinline__ float pass1_fast(const bf16x8 (&kf)[KB][D / 16], const bf16x8 (&qf)[D / 16], float c,
-                                            float& ref) {
+                                            float run, float& ref) {
     constexpr int KS = D / 16;
     f32x16 cur = logits<KS>(kf[0], qf);
-    ref = cur[0] * c;
+    ref = run > kNegBig ? run : cur[0] * c;
     float zs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
