@@ -4,9 +4,11 @@
  * C ABI of libkvsel.so. Every pointer argument named as device memory must be
  * memory the caller allocated on the current HIP device (hipMalloc, or a torch
  * tensor); the library never allocates, frees or keeps a pointer after a call
- * returns, and it holds no mutable global state. Work is enqueued on the
- * caller's HIP stream (`stream` is a hipStream_t; NULL means the default
- * stream) and runs asynchronously; calls on one stream run in order.
+ * returns. Its only mutable global state is kvsel_topk_noalloc's per-GPU
+ * scratch array and the cached address of that array (described there).
+ * Work is enqueued on the caller's HIP stream (`stream` is a hipStream_t;
+ * NULL means the default stream) and runs asynchronously; calls on one
+ * stream run in order.
  *
  * Errors are return codes. Arguments are validated on the host before any
  * launch; when a call returns anything but KVSEL_OK nothing was enqueued and
